@@ -1,0 +1,25 @@
+"""CPU fp64 oracle for the Lightning Attention layer.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the product path.  It shares no code
+with the HIP library.
+
+Two independent evaluations of the same definition
+(o_t = sum_{s<=t} lambda^(t-s) (q_t . k_s) v_s + lambda^(t+1) q_t^T S0,
+lambda = exp(-slope), Ling & Ring 2.6 Technical Report pages, "Hybrid Linear
+Attention" and "Context Parallel for Lightning Attention" sections):
+
+* `fwd`, `decode`, `bwd`, `fwd_chunked` call the plain C recurrent code in
+  `la_oracle.c` (fp64, OpenMP over (b, h));
+* `brute` holds the quadratic (masked-matrix) forms in numpy, for tiny sizes.
+"""
+from .core import (  # noqa: F401
+    build,
+    fwd,
+    fwd_chunked,
+    decode,
+    bwd,
+    num_threads,
+    library_path,
+)
+from . import brute  # noqa: F401

@@ -1,0 +1,125 @@
+"""ctypes wrapper around the C recurrent oracle (la_oracle.c).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  All arrays are converted
+to contiguous float64 before the call; the slope stays fp32, the exact values
+handed to the GPU, and the decay is exp(-(double)slope) inside the C code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "la_oracle.c")
+_LIB = os.path.join(_HERE, "liblaoracle.so")
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB
+
+
+def build(force: bool = False) -> str:
+    """Compile la_oracle.c with gcc (-O2, OpenMP).  Plain C, no GPU code."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", _SRC, "-o", tmp, "-lm"]
+        )
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        lib.lao_fwd.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
+        lib.lao_fwd_chunked.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P]
+        lib.lao_decode.argtypes = [I, I, I, P, P, P, P, P, P]
+        lib.lao_bwd.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P, P]
+        lib.lao_num_threads.restype = I
+        for f in (lib.lao_fwd, lib.lao_fwd_chunked, lib.lao_decode, lib.lao_bwd):
+            f.restype = None
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _slope(s):
+    return np.ascontiguousarray(s, dtype=np.float32)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def num_threads() -> int:
+    return _load().lao_num_threads()
+
+
+def fwd(q, k, v, slope, S0=None):
+    """Recurrent forward.  q, k, v: [B,H,N,d]; slope: [H]; S0: [B,H,d,d] or None.
+
+    Returns (o [B,H,N,d], S_N [B,H,d,d]) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    s = _slope(slope)
+    assert s.shape == (H,)
+    S0 = None if S0 is None else _f64(S0)
+    if S0 is not None:
+        assert S0.shape == (B, H, d, d)
+    o = np.empty_like(q)
+    S = np.empty((B, H, d, d), dtype=np.float64)
+    _load().lao_fwd(B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(S0), _ptr(o), _ptr(S))
+    return o, S
+
+
+def fwd_chunked(q, k, v, slope, C, S0=None):
+    """Chunked-order forward (same definition, different evaluation order)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    s = _slope(slope)
+    S0 = None if S0 is None else _f64(S0)
+    o = np.empty_like(q)
+    S = np.empty((B, H, d, d), dtype=np.float64)
+    _load().lao_fwd_chunked(
+        B, H, N, d, int(C), _ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(S0), _ptr(o), _ptr(S)
+    )
+    return o, S
+
+
+def decode(q, k, v, slope, state):
+    """One decode step.  q, k, v: [B,H,d]; state: [B,H,d,d] (not modified).
+
+    Returns (o [B,H,d], new_state [B,H,d,d])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, d = q.shape
+    s = _slope(slope)
+    st = np.array(state, dtype=np.float64, copy=True, order="C")
+    o = np.empty_like(q)
+    _load().lao_decode(B, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(st), _ptr(o))
+    return o, st
+
+
+def bwd(q, k, v, dout, slope, S0=None):
+    """Gradients (dq, dk, dv) of L = sum(o * dout)."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, d = q.shape
+    s = _slope(slope)
+    S0 = None if S0 is None else _f64(S0)
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    _load().lao_bwd(
+        B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s), _ptr(S0), _ptr(dq), _ptr(dk), _ptr(dv)
+    )
+    return dq, dk, dv
