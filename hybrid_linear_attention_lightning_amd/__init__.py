@@ -1,0 +1,188 @@
+"""Lightning Attention for AMD Instinct MI355X (gfx950).
+
+Python binding of the C ABI in include/lightning_la.h: argument marshalling
+only.  Every step of the computation runs in the HIP kernels of
+liblightning_la.so; there is no CPU or PyTorch fallback, and importing this
+module fails loudly if the library cannot be built or loaded.  PyTorch is used
+for device memory (tensors) and streams.
+
+    o, S = prefill(q, k, v, slope, chunk=128)        # q, k, v: [B, H, N, d] cuda tensors
+    o    = decode_step(q1, k1, v1, slope, S)          # S updated in place
+    dq, dk, dv = prefill_bwd(q, k, v, dout, slope, chunk=64)
+
+The operation (Ling & Ring 2.6 Technical Report pages, "Hybrid Linear
+Attention" section): per head, lambda = exp(-slope[h]),
+S_t = lambda S_{t-1} + k_t v_t^T and o_t = q_t^T S_t.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime this library links against
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblightning_la.so")
+
+LA_F32, LA_BF16 = 0, 1
+STATUS = {
+    0: "LA_OK",
+    1: "LA_ERR_NULL_POINTER",
+    2: "LA_ERR_BAD_SHAPE",
+    3: "LA_ERR_BAD_DTYPE",
+    4: "LA_ERR_UNSUPPORTED",
+    5: "LA_ERR_WORKSPACE",
+    6: "LA_ERR_HIP",
+    7: "LA_ERR_ALIGNMENT",
+    8: "LA_ERR_ALIAS",
+}
+
+# every symbol the header declares, with its ctypes signature
+_P, _I, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = {
+    "la_prefill": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "la_decode_step": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
+    "la_prefill_bwd": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "la_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
+    "la_status_string": (ctypes.c_char_p, [_I]),
+    "la_abi_version": (_I, []),
+}
+
+_lib = None
+
+
+class LightningError(RuntimeError):
+    def __init__(self, fn, code, lib):
+        msg = lib.la_status_string(code).decode() if lib is not None else ""
+        super().__init__("%s failed: %s (%s)" % (fn, STATUS.get(code, code), msg))
+        self.code = code
+
+
+def lib():
+    """The loaded liblightning_la.so (built in-tree first if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _build
+
+            _build.build()
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(handle, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(fn, code):
+    if code != 0:
+        raise LightningError(fn, code, _lib)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    if t.dtype == torch.float32:
+        return LA_F32
+    raise TypeError("expected bfloat16 or float32 tensors, got %s" % t.dtype)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def workspace_bytes(op: int, dtype: int, B: int, H: int, N: int, d: int, C: int) -> int:
+    n = lib().la_workspace_bytes(op, dtype, B, H, N, d, C)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("arguments rejected by la_workspace_bytes")
+    return n
+
+
+def _workspace(nbytes: int, device, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is None or ws.numel() * ws.element_size() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def prefill(q, k, v, slope, chunk=64, state_in=None, out=None, state_out=None,
+            return_state=True, workspace=None, stream=None):
+    """Chunked forward.  q, k, v: [B,H,N,d] bf16 or fp32; slope: [H] fp32.
+
+    Returns (o, state_out) where state_out is [B,H,d,d] fp32 (None when
+    return_state is False and no state_out tensor is given)."""
+    B, H, N, d = q.shape
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("%s must match q in shape and dtype" % name)
+    if out is None:
+        out = torch.empty_like(q)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    nbytes = workspace_bytes(0, dt, B, H, N, d, chunk)
+    ws, wsb = _workspace(nbytes, q.device, workspace)
+    code = lib().la_prefill(
+        dt, B, H, N, d, chunk,
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(slope, "slope", torch.float32),
+        None if state_in is None else _dev(state_in, "state_in", torch.float32),
+        _dev(out, "out", q.dtype),
+        None if state_out is None else _dev(state_out, "state_out", torch.float32),
+        None if ws is None else ws.data_ptr(), wsb, _stream(stream),
+    )
+    _check("la_prefill", code)
+    return out, state_out
+
+
+def decode_step(q, k, v, slope, state, out=None, stream=None):
+    """One decode step.  q, k, v: [B,H,d]; state: [B,H,d,d] fp32 updated in place."""
+    B, H, d = q.shape
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    code = lib().la_decode_step(
+        dt, B, H, d, _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+        _dev(slope, "slope", torch.float32), _dev(state, "state", torch.float32),
+        _dev(out, "out", q.dtype), _stream(stream),
+    )
+    _check("la_decode_step", code)
+    return out
+
+
+def prefill_bwd(q, k, v, dout, slope, chunk=64, dq=None, dk=None, dv=None,
+                workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(o * dout) for o = prefill(q, k, v, slope)."""
+    B, H, N, d = q.shape
+    dt = _dtype_code(q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    nbytes = workspace_bytes(1, dt, B, H, N, d, chunk)
+    ws, wsb = _workspace(nbytes, q.device, workspace)
+    code = lib().la_prefill_bwd(
+        dt, B, H, N, d, chunk,
+        _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(dout, "dout", q.dtype),
+        _dev(slope, "slope", torch.float32), None,
+        _dev(dq, "dq", q.dtype), _dev(dk, "dk", q.dtype), _dev(dv, "dv", q.dtype),
+        None if ws is None else ws.data_ptr(), wsb, _stream(stream),
+    )
+    _check("la_prefill_bwd", code)
+    return dq, dk, dv
+
+
+def abi_version() -> int:
+    return lib().la_abi_version()

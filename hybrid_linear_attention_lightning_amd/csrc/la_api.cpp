@@ -1,0 +1,265 @@
+// la_api.cpp -- the C ABI (include/lightning_la.h): argument validation,
+// execution plan, launches on the caller's stream.
+//
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing and needs no GPU.  No exception crosses the boundary.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/lightning_la.h"
+#include "la_internal.h"
+
+namespace {
+
+// Workgroups the bf16 prefill aims for: one per compute unit of an MI355X
+// (256 CUs).  Fixed, so that la_workspace_bytes needs no device query.
+constexpr int kTargetWorkgroups = 256;
+// Upper bound on a piece of the segment pre-pass (tokens).
+constexpr int kMaxPieceLen = 1024;
+
+struct Plan {
+  int nseg = 1, seg_len = 0, piece_len = 0, npiece = 0;
+  size_t pieces_bytes = 0, seg_bytes = 0;
+  size_t ws() const { return pieces_bytes + seg_bytes; }
+};
+
+bool d_ok(la_dtype_t dt, int d) {
+  if (dt == LA_BF16) return d == 64 || d == 128;
+  return d == 16 || d == 32 || d == 64 || d == 128;
+}
+bool c_ok(int C) { return C == 16 || C == 32 || C == 64 || C == 128; }
+
+Plan make_plan(la_dtype_t dt, int B, int H, int N, int d, int C) {
+  Plan p;
+  if (dt != LA_BF16) {
+    p.seg_len = N;
+    return p;
+  }
+  const long long heads = (long long)B * H;
+  const int nchunks = (N + C - 1) / C;
+  int nseg = 1;
+  if (heads < kTargetWorkgroups) nseg = (int)((kTargetWorkgroups + heads - 1) / heads);
+  if (nseg > nchunks) nseg = nchunks;
+  const int seg_chunks = (nchunks + nseg - 1) / nseg;
+  nseg = (nchunks + seg_chunks - 1) / seg_chunks;
+  p.nseg = nseg;
+  p.seg_len = seg_chunks * C;
+  if (nseg > 1) {
+    int pc = 1;
+    for (int x = 1; x <= seg_chunks; ++x)
+      if (seg_chunks % x == 0 && (long long)x * C <= kMaxPieceLen) pc = x;
+    p.piece_len = pc * C;
+    p.npiece = (nseg - 1) * (seg_chunks / pc);
+    const size_t dd = (size_t)d * d * sizeof(float);
+    p.pieces_bytes = (size_t)heads * p.npiece * dd;
+    p.seg_bytes = (size_t)heads * nseg * dd;
+  }
+  return p;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+la_status_t hip_status(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_HIP; }
+
+// Shape checks shared by prefill and its backward.
+la_status_t check_seq(la_dtype_t dt, int B, int H, int N, int d, int C) {
+  if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_BAD_DTYPE;
+  if (B < 1 || H < 1 || N < 1 || !d_ok(dt, d) || !c_ok(C)) return LA_ERR_BAD_SHAPE;
+  if (dt == LA_BF16 && C < 32) return LA_ERR_UNSUPPORTED;
+  // int indexing of grids and token offsets inside the kernels
+  if ((long long)B * H * N > (1LL << 31) / 2) return LA_ERR_UNSUPPORTED;
+  return LA_OK;
+}
+
+// One causal (or, with reverse, anti-causal) pass with its segment pre-pass.
+la_status_t run_pass(la_dtype_t dt, const Plan& pl, int B, int H, int N, int d, int C,
+                     const void* q, const void* k, const void* v, const float* slope,
+                     const float* state_in, void* o, float* state_out, bool reverse,
+                     void* workspace, hipStream_t s) {
+  la::FwdPass fp{};
+  fp.q = q;
+  fp.k = k;
+  fp.v = v;
+  fp.o = o;
+  fp.slope = slope;
+  fp.state_in = state_in;
+  fp.state_out = state_out;
+  fp.B = B;
+  fp.H = H;
+  fp.N = N;
+  fp.D = d;
+  fp.C = C;
+  fp.reverse = reverse;
+  fp.seg_len = pl.seg_len;
+  fp.nseg = pl.nseg;
+  if (dt == LA_F32) return hip_status(la::launch_fwd_f32(fp, s));
+  if (pl.nseg > 1) {
+    float* pieces = (float*)workspace;
+    float* seg_states = (float*)((char*)workspace + pl.pieces_bytes);
+    la::PiecePass pp{};
+    pp.k = k;
+    pp.v = v;
+    pp.slope = slope;
+    pp.pieces = pieces;
+    pp.B = B;
+    pp.H = H;
+    pp.N = N;
+    pp.D = d;
+    pp.C = C;
+    pp.reverse = reverse;
+    pp.piece_len = pl.piece_len;
+    pp.npiece = pl.npiece;
+    pp.seg_len = pl.seg_len;
+    pp.nseg = pl.nseg;
+    la_status_t st = hip_status(la::launch_pieces_bf16(pp, s));
+    if (st != LA_OK) return st;
+    la::ScanPass sp{};
+    sp.pieces = pieces;
+    sp.state_in = state_in;
+    sp.seg_states = seg_states;
+    sp.slope = slope;
+    sp.B = B;
+    sp.H = H;
+    sp.N = N;
+    sp.D = d;
+    sp.piece_len = pl.piece_len;
+    sp.npiece = pl.npiece;
+    sp.seg_len = pl.seg_len;
+    sp.nseg = pl.nseg;
+    st = hip_status(la::launch_scan(sp, s));
+    if (st != LA_OK) return st;
+    fp.seg_states = seg_states;
+  }
+  return hip_status(la::launch_fwd_bf16(fp, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status_t la_prefill(la_dtype_t dt, int B, int H, int N, int d, int C, const void* q,
+                       const void* k, const void* v, const float* slope, const float* state_in,
+                       void* o, float* state_out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  try {
+    la_status_t st = check_seq(dt, B, H, N, d, C);
+    if (st != LA_OK) return st;
+    if (!q || !k || !v || !slope || !o) return LA_ERR_NULL_POINTER;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        !aligned16(state_in) || !aligned16(state_out) || ((uintptr_t)slope & 3u))
+      return LA_ERR_ALIGNMENT;
+    const size_t esz = dt == LA_BF16 ? 2 : 4;
+    const size_t tb = (size_t)B * H * N * d * esz;
+    const size_t sb = (size_t)B * H * d * d * sizeof(float);
+    if (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb))
+      return LA_ERR_ALIAS;
+    if (state_in && state_out && state_in != state_out && overlap(state_in, sb, state_out, sb))
+      return LA_ERR_ALIAS;
+    if (state_out && (overlap(state_out, sb, q, tb) || overlap(state_out, sb, k, tb) ||
+                      overlap(state_out, sb, v, tb) || overlap(state_out, sb, o, tb)))
+      return LA_ERR_ALIAS;
+    const Plan pl = make_plan(dt, B, H, N, d, C);
+    if (pl.ws() > 0 && (!workspace || workspace_bytes < pl.ws())) return LA_ERR_WORKSPACE;
+    if (pl.ws() > 0 && !aligned16(workspace)) return LA_ERR_ALIGNMENT;
+    return run_pass(dt, pl, B, H, N, d, C, q, k, v, slope, state_in, o, state_out, false,
+                    workspace, (hipStream_t)stream);
+  } catch (...) {
+    return LA_ERR_HIP;
+  }
+}
+
+la_status_t la_decode_step(la_dtype_t dt, int B, int H, int d, const void* q, const void* k,
+                           const void* v, const float* slope, float* state, void* o,
+                           void* stream) {
+  try {
+    if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_BAD_DTYPE;
+    if (B < 1 || H < 1 || !d_ok(dt, d)) return LA_ERR_BAD_SHAPE;
+    if ((long long)B * H > (1LL << 31) - 1) return LA_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !slope || !state || !o) return LA_ERR_NULL_POINTER;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) ||
+        !aligned16(o) || ((uintptr_t)slope & 3u))
+      return LA_ERR_ALIGNMENT;
+    const size_t esz = dt == LA_BF16 ? 2 : 4;
+    const size_t tb = (size_t)B * H * d * esz;
+    const size_t sb = (size_t)B * H * d * d * sizeof(float);
+    if (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb) ||
+        overlap(o, tb, state, sb) || overlap(state, sb, q, tb) || overlap(state, sb, k, tb) ||
+        overlap(state, sb, v, tb))
+      return LA_ERR_ALIAS;
+    return hip_status(la::launch_decode(dt == LA_BF16, B, H, d, q, k, v, slope, state, o,
+                                        (hipStream_t)stream));
+  } catch (...) {
+    return LA_ERR_HIP;
+  }
+}
+
+la_status_t la_prefill_bwd(la_dtype_t dt, int B, int H, int N, int d, int C, const void* q,
+                           const void* k, const void* v, const void* dout, const float* slope,
+                           const float* state_in, void* dq, void* dk, void* dv,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    la_status_t st = check_seq(dt, B, H, N, d, C);
+    if (st != LA_OK) return st;
+    if (!q || !k || !v || !dout || !slope || !dq || !dk || !dv) return LA_ERR_NULL_POINTER;
+    if (state_in) return LA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)slope & 3u))
+      return LA_ERR_ALIGNMENT;
+    const size_t esz = dt == LA_BF16 ? 2 : 4;
+    const size_t tb = (size_t)B * H * N * d * esz;
+    const void* ins[4] = {q, k, v, dout};
+    void* outs[3] = {dq, dk, dv};
+    for (int a = 0; a < 3; ++a) {
+      for (int b = 0; b < 4; ++b)
+        if (overlap(outs[a], tb, ins[b], tb)) return LA_ERR_ALIAS;
+      for (int b = a + 1; b < 3; ++b)
+        if (overlap(outs[a], tb, outs[b], tb)) return LA_ERR_ALIAS;
+    }
+    const Plan pl = make_plan(dt, B, H, N, d, C);
+    if (pl.ws() > 0 && (!workspace || workspace_bytes < pl.ws())) return LA_ERR_WORKSPACE;
+    if (pl.ws() > 0 && !aligned16(workspace)) return LA_ERR_ALIGNMENT;
+    const hipStream_t s = (hipStream_t)stream;
+    // dq_t = S_t dout_t: the causal pass with (q, k, v) -> (dout, v, k)
+    st = run_pass(dt, pl, B, H, N, d, C, dout, v, k, slope, nullptr, dq, nullptr, false,
+                  workspace, s);
+    if (st != LA_OK) return st;
+    // dk_s = sum_{t>=s} lambda^(t-s) (v_s . dout_t) q_t: anti-causal, (v, dout, q)
+    st = run_pass(dt, pl, B, H, N, d, C, v, dout, q, slope, nullptr, dk, nullptr, true,
+                  workspace, s);
+    if (st != LA_OK) return st;
+    // dv_s = sum_{t>=s} lambda^(t-s) (k_s . q_t) dout_t: anti-causal, (k, q, dout)
+    return run_pass(dt, pl, B, H, N, d, C, k, q, dout, slope, nullptr, dv, nullptr, true,
+                    workspace, s);
+  } catch (...) {
+    return LA_ERR_HIP;
+  }
+}
+
+size_t la_workspace_bytes(int op, la_dtype_t dt, int B, int H, int N, int d, int C) {
+  if (op != 0 && op != 1) return (size_t)-1;
+  if (check_seq(dt, B, H, N, d, C) != LA_OK) return (size_t)-1;
+  return make_plan(dt, B, H, N, d, C).ws();
+}
+
+const char* la_status_string(la_status_t s) {
+  switch (s) {
+    case LA_OK: return "ok";
+    case LA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case LA_ERR_BAD_SHAPE: return "bad shape: B, H, N must be >= 1; d or C not supported";
+    case LA_ERR_BAD_DTYPE: return "bad dtype: expected LA_F32 or LA_BF16";
+    case LA_ERR_UNSUPPORTED: return "request not supported by this build";
+    case LA_ERR_WORKSPACE: return "workspace missing or smaller than la_workspace_bytes()";
+    case LA_ERR_HIP: return "a HIP launch or runtime call failed";
+    case LA_ERR_ALIGNMENT: return "a pointer is not 16-byte aligned";
+    case LA_ERR_ALIAS: return "an output overlaps an input it must not overlap";
+  }
+  return "unknown status";
+}
+
+int la_abi_version(void) { return LA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// la_common.h -- device helpers shared by the Lightning Attention HIP kernels
+// (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint32_t f2bf(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+// two fp32 -> packed bf16x2 (lo in bits 0..15), round to nearest even; on
+// gfx950 this is one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf2f(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// D = A(16x32) * B(32x16) + C on the matrix cores, bf16 inputs, fp32 accumulate.
+// Lane l holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16] and
+// D[4*(l/16) + r][l%16] for r = 0..3.
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Position of token / feature x inside its 32-block in the "fragment order"
+// used in LDS: x = 32*blk + 16*h + 4*g + r  ->  32*blk + 8*g + 4*h + r.
+// A lane of group g then reads 8 contiguous elements that are exactly the
+// rows {4g..4g+3} of two consecutive 16-row accumulator tiles, so MFMA
+// results can be fed back as operands without a transpose.
+__device__ __forceinline__ int frag_pos(int x) {
+  return (x & ~31) | (((x >> 2) & 3) << 3) | (((x >> 4) & 1) << 2) | (x & 3);
+}
+
+__device__ __forceinline__ u32x4_t lds_read16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+}  // namespace la

@@ -1,0 +1,154 @@
+// la_scan_f32.hip -- segment start states, and the fp32 reference-precision
+// forward.
+//
+// Segment start states.  The "Context Parallel for Lightning Attention"
+// section of the Ling & Ring 2.6 pages computes each shard's hidden state
+// from a zero start (local recursion) and then corrects every shard with the
+// states of the shards before it (global correction).  On one GPU the same
+// algebra gives parallelism along the sequence: with segments of L tokens and
+// pieces of Lp tokens (Lp divides L), the state entering segment r is
+//
+//   S_in(r) = lambda^L S_in(r-1) + sum_{pieces p in segment r-1}
+//                                  lambda^(rL - end_p) P_p,       S_in(0) = S0
+//
+// where P_p = sum_{t in p} lambda^(end_p - 1 - t) k_t v_t^T and end_p is one
+// past the piece's last token.  A piece whose decay to the next segment start
+// is below 2^-kSkipLog2 is neither computed nor added (its contribution is
+// below fp32 resolution by a factor of more than 2^40).
+//
+// fp32 forward.  The chunked recursion evaluated with fp32 FMAs on the vector
+// units, one workgroup per (b, h), chunks of at most 64 (d <= 64) or 32
+// (d = 128) rows so that Q, K, V, the scores and the d x d state fit in LDS.
+#include "la_common.h"
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+__global__ __launch_bounds__(256) void scan_kernel(ScanPass p) {
+  // grid: (B*H) x (D*D/4/256 blocks); each thread owns one float4 of the state
+  const int D = p.D;
+  const int per_head = D * D / 4;
+  const int bh = blockIdx.x / ((per_head + 255) / 256);
+  const int e4 = (blockIdx.x % ((per_head + 255) / 256)) * 256 + threadIdx.x;
+  if (e4 >= per_head) return;
+  const int h = bh % p.H;
+  const float sl2 = p.slope[h] * kLog2e;
+  const size_t dd = (size_t)D * D;
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+  if (p.state_in) s = reinterpret_cast<const f32x4_t*>(p.state_in + bh * dd)[e4];
+  const float gL = exp2f(-sl2 * (float)p.seg_len);
+  const int ppseg = p.seg_len / p.piece_len;
+  for (int r = 1; r < p.nseg; ++r) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s[c] *= gL;
+    const int start = r * p.seg_len;
+    for (int pc = (r - 1) * ppseg; pc < r * ppseg; ++pc) {
+      const int end = min(p.N, (pc + 1) * p.piece_len);
+      const float gap = (float)(start - end);
+      if (sl2 * gap >= kSkipLog2) continue;  // piece was not computed
+      const float f = exp2f(-sl2 * gap);
+      const f32x4_t v =
+          reinterpret_cast<const f32x4_t*>(p.pieces + ((size_t)bh * p.npiece + pc) * dd)[e4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) s[c] = fmaf(f, v[c], s[c]);
+    }
+    reinterpret_cast<f32x4_t*>(p.seg_states + ((size_t)bh * p.nseg + r) * dd)[e4] = s;
+  }
+}
+
+template <int D, int CS>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(FwdPass p) {
+  constexpr int DS = D + 1;  // padded row stride
+  __shared__ float Sm[D * D];
+  __shared__ float Qm[CS * DS], Km[CS * DS], Vm[CS * DS];
+  __shared__ float Pm[CS * (CS + 1)];
+  __shared__ float bj[CS];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int h = bh % p.H;
+  const int N = p.N;
+  const float sl2 = p.slope[h] * kLog2e;
+  const size_t head_off = (size_t)bh * N * D;
+  const float* qg = (const float*)p.q + head_off;
+  const float* kg = (const float*)p.k + head_off;
+  const float* vg = (const float*)p.v + head_off;
+  float* og = (float*)p.o + head_off;
+  for (int e = tid; e < D * D; e += 256)
+    Sm[e] = p.state_in ? p.state_in[(size_t)bh * D * D + e] : 0.f;
+  auto tok = [&](int tau) { return p.reverse ? (N - 1 - tau) : tau; };
+  for (int t0 = 0; t0 < N; t0 += CS) {
+    const int n = min(CS, N - t0);
+    __syncthreads();
+    for (int e = tid; e < CS * D; e += 256) {
+      const int r = e / D, c = e % D;
+      const bool ok = r < n;
+      const size_t g = ok ? (size_t)tok(t0 + r) * D + c : 0;
+      Qm[r * DS + c] = ok ? qg[g] : 0.f;
+      Km[r * DS + c] = ok ? kg[g] : 0.f;
+      Vm[r * DS + c] = ok ? vg[g] : 0.f;
+    }
+    __syncthreads();
+    for (int e = tid; e < CS * CS; e += 256) {
+      const int i = e / CS, j = e % CS;
+      float acc = 0.f;
+      if (j <= i) {
+        for (int x = 0; x < D; ++x) acc = fmaf(Qm[i * DS + x], Km[j * DS + x], acc);
+        acc *= exp2f(-sl2 * (float)(i - j));
+      }
+      Pm[i * (CS + 1) + j] = acc;
+    }
+    __syncthreads();
+    for (int e = tid; e < CS * D; e += 256) {
+      const int i = e / D, c = e % D;
+      if (i >= n) continue;
+      float intra = 0.f, inter = 0.f;
+      for (int j = 0; j <= i; ++j) intra = fmaf(Pm[i * (CS + 1) + j], Vm[j * DS + c], intra);
+      for (int x = 0; x < D; ++x) inter = fmaf(Qm[i * DS + x], Sm[x * D + c], inter);
+      og[(size_t)tok(t0 + i) * D + c] = intra + exp2f(-sl2 * (float)(i + 1)) * inter;
+    }
+    __syncthreads();
+    const float g = exp2f(-sl2 * (float)n);
+    if (tid < CS) bj[tid] = tid < n ? exp2f(-sl2 * (float)(n - 1 - tid)) : 0.f;
+    __syncthreads();
+    for (int e = tid; e < D * D; e += 256) {
+      const int x = e / D, c = e % D;
+      float acc = 0.f;
+      for (int j = 0; j < n; ++j) acc = fmaf(bj[j] * Km[j * DS + x], Vm[j * DS + c], acc);
+      Sm[e] = fmaf(g, Sm[e], acc);
+    }
+  }
+  __syncthreads();
+  if (p.state_out)
+    for (int e = tid; e < D * D; e += 256) p.state_out[(size_t)bh * D * D + e] = Sm[e];
+}
+
+template <int D, int CS>
+hipError_t launch_f32(const FwdPass& p, hipStream_t s) {
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CS>), dim3((unsigned)(p.B * p.H)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scan(const ScanPass& p, hipStream_t s) {
+  const int per_head = p.D * p.D / 4;
+  const unsigned grid = (unsigned)(p.B * p.H * ((per_head + 255) / 256));
+  hipLaunchKernelGGL(scan_kernel, dim3(grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// Chunks are evaluated in blocks of at most min(C, 64) rows (32 for d = 128);
+// the result does not depend on the blocking beyond rounding.
+hipError_t launch_fwd_f32(const FwdPass& p, hipStream_t s) {
+  const int cs = p.C;
+  switch (p.D) {
+    case 16: return cs >= 64 ? launch_f32<16, 64>(p, s) : cs >= 32 ? launch_f32<16, 32>(p, s) : launch_f32<16, 16>(p, s);
+    case 32: return cs >= 64 ? launch_f32<32, 64>(p, s) : cs >= 32 ? launch_f32<32, 32>(p, s) : launch_f32<32, 16>(p, s);
+    case 64: return cs >= 64 ? launch_f32<64, 64>(p, s) : cs >= 32 ? launch_f32<64, 32>(p, s) : launch_f32<64, 16>(p, s);
+    case 128: return cs >= 32 ? launch_f32<128, 32>(p, s) : launch_f32<128, 16>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace la

@@ -1,0 +1,151 @@
+/*
+ * lightning_la.h -- C ABI of the Lightning Attention layer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation.  Lightning Attention is the linear-attention half of the 7:1
+ * Lightning-Attention / MLA hybrid described in the Ling & Ring 2.6 Technical
+ * Report ("Hybrid Linear Attention: Balancing Long-Context Efficiency and Model
+ * Quality": sequence cost O(n) instead of O(n^2), for training and decoding;
+ * "Long-Context Training: Context Parallel for Lightning Attention": a
+ * recursive hidden state along the sequence).  Per batch row b and head h,
+ * with decay lambda_h = exp(-slope[h]):
+ *
+ *     S_t = lambda_h S_{t-1} + k_t v_t^T          (S_{-1} = state_in, d x d)
+ *     o_t = q_t^T S_t                              (o_t[j] = sum_i q_t[i] S_t[i][j])
+ *
+ * i.e. o_t = sum_{s<=t} lambda^(t-s) (q_t . k_s) v_s + lambda^(t+1) q_t^T S_{-1}.
+ * The current token is included with weight lambda^0 = 1.  No softmax, no
+ * normalisation, no feature map and no extra 1/sqrt(d) scale are applied.
+ *
+ * Layouts (row-major, contiguous, no strides):
+ *   token tensors q, k, v, o, dout, dq, dk, dv : [B][H][N][d]
+ *   state tensors                               : [B][H][d][d] fp32, S[i][j] with
+ *                                                 i the key feature, j the value feature
+ *   slope                                       : [H] fp32
+ *
+ * Ownership and threading.  Every pointer argument (except the status
+ * strings) is a DEVICE pointer owned by the caller.  The library allocates no
+ * device memory, keeps no pointer after a call returns and holds no mutable
+ * global state.  Work is enqueued on `stream` (a hipStream_t passed as void*;
+ * NULL is the null stream) and the call returns without synchronising.  Calls
+ * on different streams that write the same buffers race.
+ *
+ * Errors.  Arguments are validated before any HIP call; a failed check returns
+ * its code and enqueues nothing.  A launch failure returns LA_ERR_HIP.  No C++
+ * exception crosses this boundary.
+ */
+#ifndef LIGHTNING_LA_H
+#define LIGHTNING_LA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_ABI_VERSION 1
+
+typedef enum {
+  LA_OK = 0,
+  LA_ERR_NULL_POINTER = 1, /* a required pointer is NULL                       */
+  LA_ERR_BAD_SHAPE = 2,    /* B, H, N < 1, or d / C outside the supported set  */
+  LA_ERR_BAD_DTYPE = 3,    /* dtype is not LA_F32 or LA_BF16                   */
+  LA_ERR_UNSUPPORTED = 4,  /* valid request this build does not implement      */
+  LA_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required       */
+  LA_ERR_HIP = 6,          /* a HIP launch or runtime call failed              */
+  LA_ERR_ALIGNMENT = 7,    /* a pointer is not 16-byte aligned                 */
+  LA_ERR_ALIAS = 8         /* an output aliases an input it must not alias     */
+} la_status_t;
+
+typedef enum {
+  LA_F32 = 0,  /* fp32 token tensors, fp32 arithmetic                           */
+  LA_BF16 = 1  /* bf16 token tensors, fp32 accumulation and fp32 state;
+                  bf16 outputs are rounded to nearest-even from fp32            */
+} la_dtype_t;
+
+/* ------------------------------------------------------------------------ *
+ * la_prefill -- chunked forward over N tokens.
+ *
+ * Computes o for every token and, if state_out != NULL, the state after the
+ * last token.  The sequence is processed in chunks of C tokens: within a
+ * chunk the masked scores (Q K^T weighted by lambda^(i-j), j <= i) multiply V,
+ * and the chunk reads the d x d state carried from the previous chunks (the
+ * evaluation order described on the "Context Parallel for Lightning
+ * Attention" section: a local recursion, unfolded into matrix form, plus the
+ * carried state).  C changes only the rounding, never the result.
+ *
+ *   dt        LA_F32 or LA_BF16 (type of q, k, v, o)
+ *   B, H, N   >= 1;  d in {64, 128} (LA_F32 also allows 16 and 32)
+ *   C         chunk length in {16, 32, 64, 128}; N need not be a multiple of C
+ *   q, k, v   [B][H][N][d] of dt, 16-byte aligned
+ *   slope     [H] fp32, the decay is exp(-slope[h]); any finite slope >= 0
+ *   state_in  [B][H][d][d] fp32, or NULL for a zero initial state
+ *   o         [B][H][N][d] of dt, written; must not overlap q, k or v
+ *   state_out [B][H][d][d] fp32 or NULL; may equal state_in (continuation
+ *             in place) but must not partially overlap it
+ *   workspace device scratch of at least la_workspace_bytes(0, ...) bytes
+ *             (may be NULL when that is 0)
+ * ------------------------------------------------------------------------ */
+la_status_t la_prefill(la_dtype_t dt, int B, int H, int N, int d, int C,
+                       const void *q, const void *k, const void *v,
+                       const float *slope, const float *state_in, void *o,
+                       float *state_out, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ *
+ * la_decode_step -- one generated token per (b, h), on a carried state.
+ *
+ * S <- lambda S + k v^T, then o = q^T S (the update comes first, so the new
+ * token contributes with weight 1).  This is the recurrent form of the same
+ * operation used for decoding ("Hybrid Linear Attention" section: O(n)
+ * training and decoding).
+ *
+ *   q, k, v   [B][H][d] of dt
+ *   slope     [H] fp32
+ *   state     [B][H][d][d] fp32, read and written in place
+ *   o         [B][H][d] of dt, written; must not overlap q, k, v or state
+ * ------------------------------------------------------------------------ */
+la_status_t la_decode_step(la_dtype_t dt, int B, int H, int d, const void *q,
+                           const void *k, const void *v, const float *slope,
+                           float *state, void *o, void *stream);
+
+/* ------------------------------------------------------------------------ *
+ * la_prefill_bwd -- gradients of L = sum_t o_t . dout_t with respect to q, k
+ * and v (training; the pages train the layer at up to 256K context).
+ *
+ *   dq_t = S_t dout_t
+ *   dk_s = sum_{t>=s} lambda^(t-s) (dout_t . v_s) q_t
+ *   dv_s = sum_{t>=s} lambda^(t-s) (q_t . k_s) dout_t
+ *
+ * No gradient is produced for slope or for an initial state; state_in must be
+ * NULL in this version (LA_ERR_UNSUPPORTED otherwise).
+ *   dt, B, H, N, d, C, q, k, v, slope : as for la_prefill
+ *   dout       [B][H][N][d] of dt
+ *   dq, dk, dv [B][H][N][d] of dt, written; must not overlap any input or
+ *              each other
+ *   workspace  at least la_workspace_bytes(1, ...) bytes
+ * ------------------------------------------------------------------------ */
+la_status_t la_prefill_bwd(la_dtype_t dt, int B, int H, int N, int d, int C,
+                           const void *q, const void *k, const void *v,
+                           const void *dout, const float *slope,
+                           const float *state_in, void *dq, void *dk,
+                           void *dv, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Device workspace bytes needed by la_prefill (op = 0) or la_prefill_bwd
+ * (op = 1) for these sizes; 0 means NULL may be passed.  Returns (size_t)-1
+ * for arguments the corresponding call would reject. */
+size_t la_workspace_bytes(int op, la_dtype_t dt, int B, int H, int N, int d,
+                          int C);
+
+/* Static, NUL-terminated description of a status code. */
+const char *la_status_string(la_status_t status);
+
+/* LA_ABI_VERSION of the built library. */
+int la_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIGHTNING_LA_H */

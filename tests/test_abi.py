@@ -1,0 +1,106 @@
+"""The C-ABI library: it loads, exports every declared symbol, and rejects bad
+arguments before any HIP call (so these run without a GPU).
+
+Every call below is built to fail validation; none reaches a kernel launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hybrid_linear_attention_lightning_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lightning_la.h")
+
+F32, BF16 = la.LA_F32, la.LA_BF16
+OK, NULLP, SHAPE, DTYPE, UNSUP, WS, HIP, ALIGN, ALIAS = range(9)
+
+# fake, aligned, non-overlapping device addresses (never dereferenced: every
+# call here fails validation first)
+Q, K, V, O, S_IN, S_OUT, SLOPE, WSP, DO, DQ, DK, DV = (0x10_0000_0000 * (i + 1) for i in range(12))
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(la_[a-z_]+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = la.lib()
+    syms = declared_symbols()
+    assert set(syms) == set(la.SIGNATURES), syms
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_abi_version_and_status_strings():
+    lib = la.lib()
+    assert lib.la_abi_version() == 1
+    for code in range(9):
+        assert lib.la_status_string(code)
+    assert lib.la_status_string(123) == b"unknown status"
+
+
+def prefill(dt=BF16, B=1, H=2, N=256, d=128, C=64, q=Q, k=K, v=V, slope=SLOPE, s_in=None,
+            o=O, s_out=None, ws=None, wsb=0):
+    return la.lib().la_prefill(dt, B, H, N, d, C, q, k, v, slope, s_in, o, s_out, ws, wsb, None)
+
+
+def test_prefill_validation():
+    nws = la.workspace_bytes(0, BF16, 1, 2, 256, 128, 64)
+    assert nws > 0  # few heads: the sequence is split into segments
+    assert prefill(dt=7) == DTYPE
+    assert prefill(B=0) == SHAPE and prefill(H=0) == SHAPE and prefill(N=0) == SHAPE
+    assert prefill(d=96) == SHAPE and prefill(dt=BF16, d=32) == SHAPE
+    assert prefill(C=48) == SHAPE and prefill(C=256) == SHAPE
+    assert prefill(dt=BF16, C=16) == UNSUP
+    assert prefill(q=None) == NULLP and prefill(slope=None) == NULLP and prefill(o=None) == NULLP
+    assert prefill(q=Q + 8) == ALIGN and prefill(o=O + 2) == ALIGN and prefill(slope=SLOPE + 1) == ALIGN
+    assert prefill(s_in=S_IN + 4) == ALIGN
+    assert prefill(o=Q) == ALIAS and prefill(o=V + 64) == ALIAS
+    assert prefill(s_in=S_IN, s_out=S_IN + 16) == ALIAS
+    assert prefill(s_out=O) == ALIAS
+    assert prefill() == WS  # needs a workspace
+    assert prefill(ws=WSP, wsb=nws - 1) == WS
+    assert prefill(ws=WSP + 8, wsb=nws) == ALIGN
+
+
+def test_decode_validation():
+    f = la.lib().la_decode_step
+
+    def call(dt=BF16, B=2, H=2, d=128, q=Q, k=K, v=V, slope=SLOPE, st=S_IN, o=O):
+        return f(dt, B, H, d, q, k, v, slope, st, o, None)
+
+    assert call(dt=3) == DTYPE
+    assert call(B=0) == SHAPE and call(d=100) == SHAPE
+    assert call(st=None) == NULLP and call(k=None) == NULLP
+    assert call(st=S_IN + 4) == ALIGN
+    assert call(o=S_IN + 64) == ALIAS and call(st=Q) == ALIAS
+
+
+def test_backward_validation():
+    f = la.lib().la_prefill_bwd
+
+    def call(dt=BF16, N=256, C=64, s_in=None, dq=DQ, dk=DK, dv=DV, ws=None, wsb=0):
+        return f(dt, 1, 2, N, 128, C, Q, K, V, DO, SLOPE, s_in, dq, dk, dv, ws, wsb, None)
+
+    assert call(C=16) == UNSUP
+    assert call(dq=None) == NULLP
+    assert call(s_in=S_IN) == UNSUP
+    assert call(dk=DQ) == ALIAS and call(dv=DO) == ALIAS
+    assert call() == WS
+
+
+def test_workspace_plan():
+    # fp32 path and many heads: single segment, no workspace
+    assert la.workspace_bytes(0, F32, 1, 2, 256, 64, 64) == 0
+    assert la.workspace_bytes(0, BF16, 16, 16, 4096, 128, 64) == 0
+    # 128K-token prefill with 32 heads: segments and piece states
+    n = la.workspace_bytes(0, BF16, 1, 32, 131072, 128, 128)
+    assert 0 < n < 2**30
+    assert la.workspace_bytes(1, BF16, 1, 32, 131072, 128, 128) == n
+    with pytest.raises(ValueError):
+        la.workspace_bytes(0, BF16, 1, 32, 131072, 100, 128)
+    assert la.lib().la_workspace_bytes(2, BF16, 1, 1, 1, 64, 64) == ctypes.c_size_t(-1).value

@@ -1,0 +1,194 @@
+"""GPU parity of the HIP path against the fp64 CPU oracle, through the C ABI.
+
+Small shapes cover several chunks, ragged tails, every chunk length, both head
+dims, both dtypes, the segmented and single-segment plans and the degenerate
+decays.  The full-size workloads run in the same launch configuration the
+benchmark uses and are checked on sampled heads (heads are independent, so
+the oracle computes those heads exactly).
+"""
+import numpy as np
+import pytest
+import torch
+
+import la_inputs
+import hybrid_linear_attention_lightning_amd as la
+from tests._gpu import assert_close, device, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, B, H, N, d, dtype):
+    q, k, v = la_inputs.qkv(seed, B, H, N, d, dtype=dtype)
+    return q, k, v
+
+
+def _run_prefill(q, k, v, s, C, dtype, S0=None):
+    tq, tk, tv = (to_dev(x, dtype) for x in (q, k, v))
+    ts = torch.from_numpy(s).to(device())
+    tS0 = None if S0 is None else torch.from_numpy(np.ascontiguousarray(S0, dtype=np.float32)).to(device())
+    o, S = la.prefill(tq, tk, tv, ts, chunk=C, state_in=tS0)
+    torch.cuda.synchronize()
+    return to_host(o), to_host(S)
+
+
+def test_tiny_f32_workload(oracle_mod):
+    c = la_inputs.CONFIGS["tiny_f32"]
+    q, k, v = _inputs(c["seed"], c["B"], c["H"], c["N"], c["d"], "f32")
+    s = la_inputs.slopes(c["H"])
+    o, S = _run_prefill(q, k, v, s, c["C"], "f32")
+    ro, rS = oracle_mod.fwd(q, k, v, s)
+    assert_close(o, ro, "f32", "o")
+    assert_close(S, rS, "f32", "S")
+
+
+BF16_CASES = [
+    # B, H, N, d, C, with_state
+    (1, 2, 1, 128, 64, False),
+    (1, 2, 37, 128, 64, True),
+    (2, 3, 200, 128, 64, False),
+    (1, 4, 513, 128, 128, True),
+    (2, 2, 300, 128, 32, False),
+    (1, 3, 777, 64, 64, True),
+    (2, 2, 129, 64, 128, False),
+    (1, 1, 1000, 64, 32, False),
+    (16, 16, 100, 64, 64, False),  # 256 heads: single segment
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,C,with_state", BF16_CASES)
+def test_bf16_prefill(oracle_mod, B, H, N, d, C, with_state):
+    q, k, v = _inputs(100 + N, B, H, N, d, "bf16")
+    s = la_inputs.slopes(H)
+    S0 = la_inputs.decode_state(7, B, H, d) if with_state else None
+    o, S = _run_prefill(q, k, v, s, C, "bf16", S0)
+    ro, rS = oracle_mod.fwd(q, k, v, s, S0)
+    assert_close(o, ro, "bf16", "o")
+    assert_close(S, rS, "bf16", "S")
+
+
+F32_CASES = [
+    (1, 2, 1, 16, 16, False),
+    (2, 2, 70, 32, 32, True),
+    (1, 3, 300, 64, 128, True),
+    (1, 2, 100, 128, 64, False),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,C,with_state", F32_CASES)
+def test_f32_prefill(oracle_mod, B, H, N, d, C, with_state):
+    q, k, v = _inputs(200 + N, B, H, N, d, "f32")
+    s = la_inputs.slopes(H)
+    S0 = la_inputs.decode_state(8, B, H, d) if with_state else None
+    o, S = _run_prefill(q, k, v, s, C, "f32", S0)
+    ro, rS = oracle_mod.fwd(q, k, v, s, S0)
+    assert_close(o, ro, "f32", "o")
+    assert_close(S, rS, "f32", "S")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_degenerate_decays(oracle_mod, dtype):
+    # slope 0 (no decay: every earlier token counts, no piece may be skipped),
+    # a huge slope (only the current token counts) and ordinary slopes
+    B, H, N, d = 1, 4, 700, 64
+    q, k, v = _inputs(301, B, H, N, d, dtype)
+    s = np.array([0.0, 1.0e4, 2.0**-8, 0.9], dtype=np.float32)
+    o, S = _run_prefill(q, k, v, s, 64, dtype)
+    ro, rS = oracle_mod.fwd(q, k, v, s)
+    for h in range(H):
+        assert_close(o[:, h], ro[:, h], dtype, "o head %d" % h)
+        assert_close(S[:, h], rS[:, h], dtype, "S head %d" % h)
+
+
+def test_state_continuation_and_in_place(oracle_mod):
+    B, H, N1, N2, d, C = 1, 4, 300, 200, 128, 64
+    q, k, v = _inputs(302, B, H, N1 + N2, d, "bf16")
+    s = la_inputs.slopes(H)
+    dev = device()
+    tq, tk, tv = (to_dev(x, "bf16") for x in (q, k, v))
+    ts = torch.from_numpy(s).to(dev)
+    o1, S1 = la.prefill(tq[:, :, :N1].contiguous(), tk[:, :, :N1].contiguous(), tv[:, :, :N1].contiguous(), ts, chunk=C)
+    # continue in place: state_in and state_out are the same buffer
+    o2, S2 = la.prefill(tq[:, :, N1:].contiguous(), tk[:, :, N1:].contiguous(), tv[:, :, N1:].contiguous(), ts,
+                        chunk=C, state_in=S1, state_out=S1)
+    torch.cuda.synchronize()
+    ro, rS = oracle_mod.fwd(q, k, v, s)
+    assert_close(np.concatenate([to_host(o1), to_host(o2)], axis=2), ro, "bf16", "o")
+    assert_close(to_host(S2), rS, "bf16", "S")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_steps(oracle_mod, dtype):
+    B, H, d, steps = 3, 4, 128 if dtype == "bf16" else 64, 5
+    s = la_inputs.slopes(H)
+    S0 = la_inputs.decode_state(9, B, H, d)
+    dev = device()
+    tS = torch.from_numpy(S0).to(dev)
+    ts = torch.from_numpy(s).to(dev)
+    ref = S0.astype(np.float64)
+    for t in range(steps):
+        q, k, v = (x[:, :, 0] for x in la_inputs.qkv(9, B, H, 1, d, dtype=dtype, step=t))
+        o = la.decode_step(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), ts, tS)
+        torch.cuda.synchronize()
+        ro, ref = oracle_mod.decode(q, k, v, s, ref)
+        assert_close(to_host(o), ro, dtype, "o step %d" % t)
+    assert_close(to_host(tS), ref, dtype, "state")
+
+
+def test_prefill_then_decode_equals_longer_prefill(oracle_mod):
+    B, H, N, d, C = 2, 2, 130, 128, 64
+    q, k, v = _inputs(303, B, H, N + 1, d, "bf16")
+    s = la_inputs.slopes(H)
+    dev = device()
+    tq, tk, tv = (to_dev(x, "bf16") for x in (q, k, v))
+    ts = torch.from_numpy(s).to(dev)
+    _, S = la.prefill(tq[:, :, :N].contiguous(), tk[:, :, :N].contiguous(), tv[:, :, :N].contiguous(), ts, chunk=C)
+    o = la.decode_step(tq[:, :, N].contiguous(), tk[:, :, N].contiguous(), tv[:, :, N].contiguous(), ts, S)
+    torch.cuda.synchronize()
+    ro, rS = oracle_mod.fwd(q, k, v, s)
+    assert_close(to_host(o), ro[:, :, N], "bf16", "o")
+    assert_close(to_host(S), rS, "bf16", "S")
+
+
+BWD_CASES = [
+    ("bf16", 1, 2, 200, 128, 64),
+    ("bf16", 2, 2, 333, 64, 128),
+    ("bf16", 1, 3, 97, 128, 32),
+    ("f32", 1, 2, 150, 64, 64),
+    ("f32", 1, 2, 64, 16, 16),
+]
+
+
+@pytest.mark.parametrize("dtype,B,H,N,d,C", BWD_CASES)
+def test_backward(oracle_mod, dtype, B, H, N, d, C):
+    q, k, v = _inputs(400 + N, B, H, N, d, dtype)
+    g = la_inputs.upstream_grad(400 + N, B, H, N, d, dtype=dtype)
+    s = la_inputs.slopes(H)
+    tq, tk, tv, tg = (to_dev(x, dtype) for x in (q, k, v, g))
+    dq, dk, dv = la.prefill_bwd(tq, tk, tv, tg, torch.from_numpy(s).to(device()), chunk=C)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle_mod.bwd(q, k, v, g, s)
+    assert_close(to_host(dq), rq, dtype, "dq")
+    assert_close(to_host(dk), rk, dtype, "dk")
+    assert_close(to_host(dv), rv, dtype, "dv")
+
+
+def test_bitwise_deterministic():
+    B, H, N, d, C = 1, 8, 2048, 128, 128
+    q, k, v = _inputs(500, B, H, N, d, "bf16")
+    tq, tk, tv = (to_dev(x, "bf16") for x in (q, k, v))
+    ts = torch.from_numpy(la_inputs.slopes(H)).to(device())
+    o1, S1 = la.prefill(tq, tk, tv, ts, chunk=C)
+    o2, S2 = la.prefill(tq, tk, tv, ts, chunk=C)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_chunk_length_changes_only_rounding(oracle_mod):
+    B, H, N, d = 1, 4, 1000, 128
+    q, k, v = _inputs(501, B, H, N, d, "bf16")
+    s = la_inputs.slopes(H)
+    ro, rS = oracle_mod.fwd(q, k, v, s)
+    for C in (32, 64, 128):
+        o, S = _run_prefill(q, k, v, s, C, "bf16")
+        assert_close(o, ro, "bf16", "o C=%d" % C)
+        assert_close(S, rS, "bf16", "S C=%d" % C)
