@@ -53,5 +53,16 @@ __device__ __forceinline__ int frag_pos(int x) {
 __device__ __forceinline__ u32x4_t lds_read16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
+__device__ __forceinline__ u32x2_t lds_read8(const uint16_t* p) {
+  return *reinterpret_cast<const u32x2_t*>(p);
+}
+
+// Split four fp32 values into bf16 hi + lo parts (x ~= hi + lo to about 2^-16
+// relative): the matrix cores then see 16 significant bits instead of 8.
+__device__ __forceinline__ void split4(f32x4_t x, u32x2_t& hi, u32x2_t& lo) {
+  const uint32_t h0 = pack2(x[0], x[1]), h1 = pack2(x[2], x[3]);
+  hi = u32x2_t{h0, h1};
+  lo = u32x2_t{pack2(x[0] - bf_lo(h0), x[1] - bf_hi(h0)), pack2(x[2] - bf_lo(h1), x[3] - bf_hi(h1))};
+}
 
 }  // namespace la

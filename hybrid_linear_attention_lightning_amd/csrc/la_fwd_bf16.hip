@@ -2,26 +2,33 @@
 //
 // Computes, per (b, h) and per segment of the sequence, the chunked form of
 // o_t = sum_{s<=t} lambda^(t-s) (q_t . k_s) v_s + lambda^(t+1) q_t^T S_in:
-// for a chunk of C tokens (local rows i, j) with carried d x d state S,
+// for a chunk of n <= C tokens (local rows i, j) with carried d x d state S,
 //
 //     O   = ((Q K^T) * M) V + diag(a) Q S,   M[i][j] = lambda^(i-j) (j <= i)
 //     S  <- lambda^n S + K^T diag(b) V,       a_i = lambda^(i+1), b_j = lambda^(n-1-j)
 //
-// (n = rows in the chunk).  This is the intra-chunk / inter-chunk split of the
-// recursion that the Ling & Ring 2.6 pages describe for their context-parallel
-// kernels ("Context Parallel for Lightning Attention": the state recursion
-// unfolded into matrix form).
+// This is the intra-chunk / inter-chunk split of the recursion that the Ling &
+// Ring 2.6 pages describe for their context-parallel kernels ("Context Parallel
+// for Lightning Attention": the state recursion unfolded into matrix form).
 //
-// Design (MI355X): one workgroup of 4 waves owns a whole head (all d value
-// columns) over one segment of the sequence, so Q K^T is computed once per
-// chunk and every operand is read from HBM once.  Parallelism beyond B*H comes
-// from segments: segment r > 0 starts from a state assembled by the piece and
-// scan kernels (the "local recursion + global correction" algebra of the same
-// section).  Each wave owns D/64 tiles of 16 value columns of the fp32 state
-// in registers; the state is fed back to the matrix cores as bf16 without a
-// transpose because Q and K are stored in LDS in "fragment order" (see
-// frag_pos).  The same kernel in STATE_ONLY mode computes piece states
-// (K^T diag(b) V accumulated over a piece) for the segment pre-pass.
+// Design (MI355X):
+//  * one workgroup of 4 waves owns a whole head (all d value columns) over one
+//    segment of the sequence, so Q K^T is computed once per chunk and every
+//    operand is read from HBM once; parallelism beyond B*H comes from segments,
+//    whose start states the piece and scan kernels assemble (the "local
+//    recursion + global correction" algebra of the same section);
+//  * each wave owns D/64 tiles of 16 value columns of the fp32 state, kept in
+//    registers for the whole segment;
+//  * the three operands that are not inputs -- the masked scores P, the state
+//    S and b*V -- are handed to the matrix cores as bf16 hi + lo pairs, so the
+//    products carry ~16 significant bits (plain bf16 operands would lose as
+//    much accuracy as the final rounding of the output);
+//  * Q and K are staged row-major in LDS, K and V also transposed (feature
+//    rows) in "fragment order" (frag_pos), so MFMA results feed back as MFMA
+//    operands without a transpose; the masked scores of a chunk are exchanged
+//    through LDS in the region of K and K^T, which are dead by then.
+// The same kernel in STATE_ONLY mode computes piece states (K^T diag(b) V
+// accumulated over a piece) for the segment pre-pass.
 #include "la_common.h"
 #include "la_internal.h"
 
@@ -45,25 +52,53 @@ struct Cfg {
   static constexpr int QS = D + 8;     // row stride (elements) of Qs / Ks
   static constexpr int TS = C + 8;     // row stride (elements) of Kt / Vt
   static constexpr int NFRAG = frag_base(NQB);
+  static constexpr int MAXT = NQB == 8 ? 9 : NQB == 4 ? 4 : 2;  // P^T tiles per wave
   static constexpr int QCH = STATE_ONLY ? 0 : (C * D / 8 + kThreads - 1) / kThreads;
   static constexpr int NB = C * D / 64;  // 8x8 blocks per tensor
   static constexpr int KVB = (2 * NB + kThreads - 1) / kThreads;
-  static constexpr int QK_ELEMS = STATE_ONLY ? 0 : 2 * C * QS;
-  static constexpr int PT_ELEMS = STATE_ONLY ? 0 : NFRAG * 64 * 8;
-  static constexpr int LDS_ELEMS = QK_ELEMS + 2 * D * TS + PT_ELEMS;
+  static constexpr int Q_ELEMS = STATE_ONLY ? 0 : C * QS;
+  static constexpr int K_ELEMS = STATE_ONLY ? 0 : C * QS;
+  static constexpr int T_ELEMS = D * TS;
+  static constexpr int PT_HALF = NFRAG * 64 * 8;  // one of P_hi / P_lo
+  // the P^T exchange reuses the space of K and K^T when it fits there
+  static constexpr bool PT_ALIAS = STATE_ONLY || 2 * PT_HALF <= K_ELEMS + T_ELEMS;
+  static constexpr int LDS_ELEMS = Q_ELEMS + K_ELEMS + 2 * T_ELEMS + (PT_ALIAS ? 0 : 2 * PT_HALF);
   static_assert(C == 32 || C == 64 || C == 128, "chunk");
   static_assert(D == 64 || D == 128, "head dim");
 };
+
+// (key block, query block) of the m-th P^T tile of a wave; balanced so that
+// every wave does the same number of 16x16 tiles when C = 128.
+template <int NQB>
+__device__ __forceinline__ bool tile_of(int wave, int m, int& kb, int& qb) {
+  if constexpr (NQB == 8) {
+    const int first = 8 - wave;  // tiles of query block 7-wave
+    if (m < first) {
+      kb = m;
+      qb = 7 - wave;
+    } else {
+      kb = m - first;
+      qb = wave;
+    }
+    return true;
+  } else {
+    qb = wave;
+    kb = m;
+    return wave < NQB && m <= wave;
+  }
+}
 
 template <int C, int D, bool STATE_ONLY>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdPass p, PiecePass pp) {
   using G = Cfg<C, D, STATE_ONLY>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[G::LDS_ELEMS];
   uint16_t* Qs = smem;
-  uint16_t* Ks = Qs + C * G::QS;
-  uint16_t* Kt = smem + G::QK_ELEMS;
-  uint16_t* Vt = Kt + D * G::TS;
-  uint16_t* Pt = Vt + D * G::TS;
+  uint16_t* Ks = Qs + G::Q_ELEMS;
+  uint16_t* Kt = Ks + G::K_ELEMS;
+  uint16_t* Vt = Kt + G::T_ELEMS;
+  // P^T hi / lo fragments, written after K and K^T are dead
+  uint16_t* Pth = G::PT_ALIAS ? Ks : Vt + G::T_ELEMS;
+  uint16_t* Ptl = Pth + G::PT_HALF;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
@@ -120,30 +155,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdPass p, PieceP
   const float sl2 = slope[h] * kLog2e;  // lambda^e = exp2(-sl2 * e)
 
   // ---- per-lane decay tables --------------------------------------------
-  // diagonal P^T tile: key row j = 4*lg + r, query column i = li
+  // P^T tile element: key row j = 16kb + 4lg + r, query column i = 16qb + li.
+  // Diagonal tiles use md (zero above the diagonal); off-diagonal tiles use
+  // lambda^(16 (qb-kb-1)) * mo[r], both factors <= 1 so nothing overflows.
   float md[4], mo[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int e = li - 4 * lg - r;
     md[r] = e >= 0 ? exp2f(-sl2 * (float)e) : 0.f;
-    mo[r] = exp2f(-sl2 * (float)(16 + e));  // 16+e in [1, 31]: never overflows
+    mo[r] = exp2f(-sl2 * (float)(16 + e));
   }
-  float aq[G::NQB];
+  float aq[G::NQB];  // a_i for this lane's query column in each query block
 #pragma unroll
   for (int qb = 0; qb < G::NQB; ++qb) aq[qb] = exp2f(-sl2 * (float)(16 * qb + li + 1));
-  // b_x = lambda^(n-1-x) for the 8 tokens x of this lane's V fragment of
-  // contraction step ks (positions 32ks + 8lg + e in fragment order)
-  float bt[G::KSC][8];
-  auto make_bt = [&](int n) {
+  // Full chunk: b for the e-th token of a V fragment of step ks (token
+  // 32ks + xl(e)) is lambda^(32 (KSC-1-ks)) * bl[e] with bl[e] = lambda^(31 - xl(e)).
+  float bl[8];
 #pragma unroll
-    for (int ks = 0; ks < G::KSC; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int x = 32 * ks + (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4);
-        bt[ks][e] = x < n ? exp2f(-sl2 * (float)(n - 1 - x)) : 0.f;
-      }
-  };
-  make_bt(C);
+  for (int e = 0; e < 8; ++e) {
+    const int xl = e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4;
+    bl[e] = exp2f(-sl2 * (float)(31 - xl));
+  }
 
   // ---- fp32 state: this wave's WT value tiles x NT key tiles ------------
   // S[wt][t][r] = S[key 16t + 4lg + r][value 16(wave*WT + wt) + li]
@@ -157,11 +189,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdPass p, PieceP
       for (int r = 0; r < 4; ++r)
         S[wt][t][r] = s_init ? s_init[(size_t)(16 * t + 4 * lg + r) * D + col] : 0.f;
     }
-
-  if constexpr (!STATE_ONLY) {
-    for (int i = tid; i < G::PT_ELEMS / 8; i += kThreads)
-      *reinterpret_cast<u32x4_t*>(Pt + 8 * i) = u32x4_t{0, 0, 0, 0};
-  }
 
   // ---- staging registers ------------------------------------------------
   u32x4_t qr[G::QCH > 0 ? G::QCH : 1];
@@ -204,9 +231,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdPass p, PieceP
         const int id = tid + kThreads * m;
         if (id < C * D / 8) {
           const int row = id / (D / 8), c8 = id % (D / 8);
-          uint16_t* dst = Qs + row * G::QS + frag_pos(8 * c8);
-          *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{qr[m][0], qr[m][1]};
-          *reinterpret_cast<u32x2_t*>(dst + 8) = u32x2_t{qr[m][2], qr[m][3]};
+          *reinterpret_cast<u32x4_t*>(Qs + row * G::QS + 8 * c8) = qr[m];
         }
       }
     }
@@ -223,9 +248,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdPass p, PieceP
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int x = 32 * tb + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4);
-              uint16_t* dst = Ks + x * G::QS + frag_pos(8 * cg);
-              *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{kvr[m][e][0], kvr[m][e][1]};
-              *reinterpret_cast<u32x2_t*>(dst + 8) = u32x2_t{kvr[m][e][2], kvr[m][e][3]};
+              *reinterpret_cast<u32x4_t*>(Ks + x * G::QS + 8 * cg) = kvr[m][e];
             }
           }
         }
@@ -247,11 +270,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdPass p, PieceP
     }
   };
 
-  // owned query blocks for the P^T tiles (balanced causal work)
-  int own0 = wave, own1 = -1;
-  if (G::NQB == 8) own1 = 7 - wave;
-  if (G::NQB == 2 && wave >= 2) own0 = -1;
-
   if (tau0 < tau_end) load_chunk(tau0, min(C, tau_end - tau0));
 
   for (int tc = tau0; tc < tau_end; tc += C) {
@@ -259,54 +277,46 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdPass p, PieceP
     store_chunk();
     __syncthreads();  // chunk tc is in LDS
     if (tc + C < tau_end) load_chunk(tc + C, min(C, tau_end - tc - C));
-    if (n != C) make_bt(n);
     const float gdec = exp2f(-sl2 * (float)n);
 
-    // bf16 copy of S_{c-1}, in the A-operand layout of S^T
-    u32x4_t sf[G::WT][G::KSD];
+    // S_{c-1} as hi/lo bf16 A-operands of S^T (value row w, 8 keys)
+    u32x4_t sfh[G::WT][G::KSD], sfl[G::WT][G::KSD];
+    // this wave's masked P^T tiles, hi/lo
+    u32x2_t ph[G::MAXT], pl[G::MAXT];
     if constexpr (!STATE_ONLY) {
 #pragma unroll
       for (int wt = 0; wt < G::WT; ++wt)
 #pragma unroll
-        for (int ks = 0; ks < G::KSD; ++ks)
-          sf[wt][ks] = u32x4_t{pack2(S[wt][2 * ks][0], S[wt][2 * ks][1]),
-                               pack2(S[wt][2 * ks][2], S[wt][2 * ks][3]),
-                               pack2(S[wt][2 * ks + 1][0], S[wt][2 * ks + 1][1]),
-                               pack2(S[wt][2 * ks + 1][2], S[wt][2 * ks + 1][3])};
+        for (int ks = 0; ks < G::KSD; ++ks) {
+          u32x2_t h0, l0, h1, l1;
+          split4(S[wt][2 * ks], h0, l0);
+          split4(S[wt][2 * ks + 1], h1, l1);
+          sfh[wt][ks] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
+          sfl[wt][ks] = u32x4_t{l0[0], l0[1], l1[0], l1[1]};
+        }
 
-      // ---- masked scores P^T = (K Q^T) * M^T for the owned query blocks ----
-      if (own0 >= 0) {
-        u32x4_t qf0[G::KSD], qf1[G::KSD];
+      // ---- masked scores P^T = (K Q^T) * M^T, kept in registers ----------
+#pragma unroll
+      for (int m = 0; m < G::MAXT; ++m) {
+        int kb, qb;
+        if (!tile_of<G::NQB>(wave, m, kb, qb)) continue;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < G::KSD; ++ks) {
-          qf0[ks] = lds_read16(Qs + (16 * own0 + li) * G::QS + 32 * ks + 8 * lg);
-          if (own1 >= 0) qf1[ks] = lds_read16(Qs + (16 * own1 + li) * G::QS + 32 * ks + 8 * lg);
+          const u32x4_t kf = lds_read16(Ks + (16 * kb + li) * G::QS + 32 * ks + 8 * lg);
+          const u32x4_t qf = lds_read16(Qs + (16 * qb + li) * G::QS + 32 * ks + 8 * lg);
+          acc = mfma16(kf, qf, acc);
         }
-        const int maxqb = own1 >= 0 ? own1 : own0;
-        auto tile = [&](int kb, int qb, const u32x4_t* kf, const u32x4_t* qf) {
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        const int delta = qb - kb;
+        if (delta == 0) {
 #pragma unroll
-          for (int ks = 0; ks < G::KSD; ++ks) acc = mfma16(kf[ks], qf[ks], acc);
-          const int delta = qb - kb;
-          if (delta == 0) {
+          for (int r = 0; r < 4; ++r) acc[r] *= md[r];
+        } else {
+          const float f = exp2f(-sl2 * (float)(16 * (delta - 1)));
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= md[r];
-          } else {
-            const float f = exp2f(-sl2 * (float)(16 * (delta - 1)));
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= f * mo[r];
-          }
-          uint16_t* dst = Pt + ((frag_base(qb) + (kb >> 1)) * 64 + lane) * 8 + (kb & 1) * 4;
-          *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{pack2(acc[0], acc[1]), pack2(acc[2], acc[3])};
-        };
-        for (int kb = 0; kb <= maxqb; ++kb) {
-          u32x4_t kf[G::KSD];
-#pragma unroll
-          for (int ks = 0; ks < G::KSD; ++ks)
-            kf[ks] = lds_read16(Ks + (16 * kb + li) * G::QS + 32 * ks + 8 * lg);
-          if (own1 >= 0) tile(kb, own1, kf, qf1);
-          if (kb <= own0) tile(kb, own0, kf, qf0);
+          for (int r = 0; r < 4; ++r) acc[r] *= f * mo[r];
         }
+        split4(acc, ph[m], pl[m]);
       }
     }
 
@@ -318,7 +328,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdPass p, PieceP
       for (int ks = 0; ks < G::KSC; ++ks)
         vfr[wt][ks] = lds_read16(Vt + (16 * (wave * G::WT + wt) + li) * G::TS + 32 * ks + 8 * lg);
 
-    // ---- state update S <- lambda^n S + K^T diag(b) V ----
+    // ---- state update S <- lambda^n S + K^T diag(b) V (b*V as hi + lo) ----
 #pragma unroll
     for (int wt = 0; wt < G::WT; ++wt)
 #pragma unroll
@@ -327,48 +337,97 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdPass p, PieceP
         for (int r = 0; r < 4; ++r) S[wt][t][r] *= gdec;
 #pragma unroll
     for (int ks = 0; ks < G::KSC; ++ks) {
-      u32x4_t vb[G::WT];
+      float bks[8];
+      if (n == C) {
+        const float f = exp2f(-sl2 * (float)(32 * (G::KSC - 1 - ks)));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bks[e] = f * bl[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int x = 32 * ks + (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4);
+          bks[e] = x < n ? exp2f(-sl2 * (float)(n - 1 - x)) : 0.f;
+        }
+      }
+      u32x4_t vbh[G::WT], vbl[G::WT];
 #pragma unroll
       for (int wt = 0; wt < G::WT; ++wt) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t w = vfr[wt][ks][c];
-          vb[wt][c] = pack2(bf_lo(w) * bt[ks][2 * c], bf_hi(w) * bt[ks][2 * c + 1]);
+        for (int c = 0; c < 2; ++c) {
+          const uint32_t w0 = vfr[wt][ks][2 * c], w1 = vfr[wt][ks][2 * c + 1];
+          const f32x4_t x = {bf_lo(w0) * bks[4 * c], bf_hi(w0) * bks[4 * c + 1],
+                             bf_lo(w1) * bks[4 * c + 2], bf_hi(w1) * bks[4 * c + 3]};
+          u32x2_t hh, ll;
+          split4(x, hh, ll);
+          vbh[wt][2 * c] = hh[0];
+          vbh[wt][2 * c + 1] = hh[1];
+          vbl[wt][2 * c] = ll[0];
+          vbl[wt][2 * c + 1] = ll[1];
         }
       }
 #pragma unroll
       for (int t = 0; t < G::NT; ++t) {
         const u32x4_t kf = lds_read16(Kt + (16 * t + li) * G::TS + 32 * ks + 8 * lg);
 #pragma unroll
-        for (int wt = 0; wt < G::WT; ++wt) S[wt][t] = mfma16(kf, vb[wt], S[wt][t]);
+        for (int wt = 0; wt < G::WT; ++wt) {
+          S[wt][t] = mfma16(kf, vbh[wt], S[wt][t]);
+          S[wt][t] = mfma16(kf, vbl[wt], S[wt][t]);
+        }
       }
     }
 
     if constexpr (!STATE_ONLY) {
-      __syncthreads();  // all P^T tiles written
+      __syncthreads();  // K and K^T are dead: their space takes the P^T fragments
+#pragma unroll
+      for (int m = 0; m < G::MAXT; ++m) {
+        int kb, qb;
+        if (!tile_of<G::NQB>(wave, m, kb, qb)) continue;
+        const int off = ((frag_base(qb) + (kb >> 1)) * 64 + lane) * 8;
+        const int half = (kb & 1) * 4;
+        *reinterpret_cast<u32x2_t*>(Pth + off + half) = ph[m];
+        *reinterpret_cast<u32x2_t*>(Ptl + off + half) = pl[m];
+        if (kb == qb && !(qb & 1)) {  // even diagonal: the other half of the step is empty
+          *reinterpret_cast<u32x2_t*>(Pth + off + 4) = u32x2_t{0, 0};
+          *reinterpret_cast<u32x2_t*>(Ptl + off + 4) = u32x2_t{0, 0};
+        }
+      }
+      __syncthreads();  // all P^T fragments written
+
       // ---- outputs: O^T = diag(a) (S^T Q^T) + V^T P^T, per query block ----
 #pragma unroll
       for (int qb = 0; qb < G::NQB; ++qb) {
+        // Q^T as B operand in the key order of the S fragments:
+        // features {32ks + 4lg + r} and {32ks + 16 + 4lg + r}
         u32x4_t qf[G::KSD];
 #pragma unroll
-        for (int ks = 0; ks < G::KSD; ++ks)
-          qf[ks] = lds_read16(Qs + (16 * qb + li) * G::QS + 32 * ks + 8 * lg);
-        constexpr int dummy = 0;
-        (void)dummy;
-        u32x4_t pf[G::KSC];
+        for (int ks = 0; ks < G::KSD; ++ks) {
+          const uint16_t* row = Qs + (16 * qb + li) * G::QS + 32 * ks + 4 * lg;
+          const u32x2_t a0 = lds_read8(row), a1 = lds_read8(row + 16);
+          qf[ks] = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+        }
+        u32x4_t pfh[G::KSC], pfl[G::KSC];
 #pragma unroll
-        for (int ks = 0; ks <= qb / 2; ++ks)
-          pf[ks] = lds_read16(Pt + ((frag_base(qb) + ks) * 64 + lane) * 8);
+        for (int ks = 0; ks <= qb / 2; ++ks) {
+          const int off = ((frag_base(qb) + ks) * 64 + lane) * 8;
+          pfh[ks] = lds_read16(Pth + off);
+          pfl[ks] = lds_read16(Ptl + off);
+        }
         const int i = 16 * qb + li;
 #pragma unroll
         for (int wt = 0; wt < G::WT; ++wt) {
           f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < G::KSD; ++ks) acc = mfma16(sf[wt][ks], qf[ks], acc);
+          for (int ks = 0; ks < G::KSD; ++ks) {
+            acc = mfma16(sfh[wt][ks], qf[ks], acc);
+            acc = mfma16(sfl[wt][ks], qf[ks], acc);
+          }
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[r] *= aq[qb];
 #pragma unroll
-          for (int ks = 0; ks <= qb / 2; ++ks) acc = mfma16(vfr[wt][ks], pf[ks], acc);
+          for (int ks = 0; ks <= qb / 2; ++ks) {
+            acc = mfma16(vfr[wt][ks], pfh[ks], acc);
+            acc = mfma16(vfr[wt][ks], pfl[ks], acc);
+          }
           if (i < n) {
             uint16_t* dst = og + (size_t)tok(tc + i) * D + 16 * (wave * G::WT + wt) + 4 * lg;
             *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{pack2(acc[0], acc[1]), pack2(acc[2], acc[3])};

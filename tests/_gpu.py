@@ -1,14 +1,22 @@
 """Shared helpers of the GPU parity tests: device transfer and the tolerances.
 
-Tolerances (the per-tensor bars; see the design doc for their derivation):
+Tolerances, per tensor:
   * fp32 inputs: max|got - ref| / max|ref| <= 1e-4 (normwise relative error);
   * bf16 inputs: max|got - ref| <= 2e-2 * rms(ref), rms over the whole tensor.
+    For tensors the library stores in bf16 (o, dq, dk, dv) the final
+    round-to-nearest of each element to bf16 is not counted as error: the
+    element test is |got - ref| - u |ref| <= 2e-2 * rms(ref) with u = 2^-8, the
+    bf16 unit roundoff.  Without that allowance the exact result itself, once
+    stored in bf16, fails the bar whenever max|ref| > 5.12 rms(ref), which the
+    mix of fast and slow heads produces (max/rms is about 11 at H = 32).
+    fp32 tensors (the state S) get no allowance.
 """
 import numpy as np
 import torch
 
 F32_TOL = 1e-4
 BF16_TOL = 2e-2
+BF16_U = 2.0**-8
 
 
 def device():
@@ -26,20 +34,29 @@ def to_host(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def err_ratio(got, ref, dtype: str) -> float:
-    """Error over the tensor's bar; <= 1 passes."""
+def err_ratio(got, ref, dtype: str, stored_bf16: bool = None) -> float:
+    """Worst element error over the tensor's bar; <= 1 passes.
+
+    stored_bf16 defaults to (dtype == "bf16") and should be False for fp32
+    outputs of the bf16 path (the state)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape
     assert np.all(np.isfinite(got)), "non-finite values"
-    err = np.max(np.abs(got - ref)) if got.size else 0.0
+    if got.size == 0:
+        return 0.0
+    if stored_bf16 is None:
+        stored_bf16 = dtype == "bf16"
     if dtype == "bf16":
-        rms = np.sqrt(np.mean(ref * ref)) if ref.size else 1.0
-        return err / (BF16_TOL * max(rms, 1e-30))
-    return err / (F32_TOL * max(np.max(np.abs(ref)), 1e-30))
+        rms = max(np.sqrt(np.mean(ref * ref)), 1e-30)
+        err = np.abs(got - ref)
+        if stored_bf16:
+            err = err - BF16_U * np.abs(ref)
+        return float(np.max(err)) / (BF16_TOL * rms)
+    return float(np.max(np.abs(got - ref))) / (F32_TOL * max(np.max(np.abs(ref)), 1e-30))
 
 
-def assert_close(got, ref, dtype: str, what: str = ""):
-    r = err_ratio(got, ref, dtype)
+def assert_close(got, ref, dtype: str, what: str = "", stored_bf16: bool = None):
+    r = err_ratio(got, ref, dtype, stored_bf16)
     assert r <= 1.0, "%s: error is %.3g of the %s bar" % (what, r, dtype)
     return r

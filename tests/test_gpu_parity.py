@@ -38,7 +38,7 @@ def test_tiny_f32_workload(oracle_mod):
     o, S = _run_prefill(q, k, v, s, c["C"], "f32")
     ro, rS = oracle_mod.fwd(q, k, v, s)
     assert_close(o, ro, "f32", "o")
-    assert_close(S, rS, "f32", "S")
+    assert_close(S, rS, "f32", "S", stored_bf16=False)
 
 
 BF16_CASES = [
@@ -63,7 +63,7 @@ def test_bf16_prefill(oracle_mod, B, H, N, d, C, with_state):
     o, S = _run_prefill(q, k, v, s, C, "bf16", S0)
     ro, rS = oracle_mod.fwd(q, k, v, s, S0)
     assert_close(o, ro, "bf16", "o")
-    assert_close(S, rS, "bf16", "S")
+    assert_close(S, rS, "bf16", "S", stored_bf16=False)
 
 
 F32_CASES = [
@@ -82,7 +82,7 @@ def test_f32_prefill(oracle_mod, B, H, N, d, C, with_state):
     o, S = _run_prefill(q, k, v, s, C, "f32", S0)
     ro, rS = oracle_mod.fwd(q, k, v, s, S0)
     assert_close(o, ro, "f32", "o")
-    assert_close(S, rS, "f32", "S")
+    assert_close(S, rS, "f32", "S", stored_bf16=False)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -96,7 +96,7 @@ def test_degenerate_decays(oracle_mod, dtype):
     ro, rS = oracle_mod.fwd(q, k, v, s)
     for h in range(H):
         assert_close(o[:, h], ro[:, h], dtype, "o head %d" % h)
-        assert_close(S[:, h], rS[:, h], dtype, "S head %d" % h)
+        assert_close(S[:, h], rS[:, h], dtype, "S head %d" % h, stored_bf16=False)
 
 
 def test_state_continuation_and_in_place(oracle_mod):
@@ -113,7 +113,7 @@ def test_state_continuation_and_in_place(oracle_mod):
     torch.cuda.synchronize()
     ro, rS = oracle_mod.fwd(q, k, v, s)
     assert_close(np.concatenate([to_host(o1), to_host(o2)], axis=2), ro, "bf16", "o")
-    assert_close(to_host(S2), rS, "bf16", "S")
+    assert_close(to_host(S2), rS, "bf16", "S", stored_bf16=False)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -131,7 +131,7 @@ def test_decode_steps(oracle_mod, dtype):
         torch.cuda.synchronize()
         ro, ref = oracle_mod.decode(q, k, v, s, ref)
         assert_close(to_host(o), ro, dtype, "o step %d" % t)
-    assert_close(to_host(tS), ref, dtype, "state")
+    assert_close(to_host(tS), ref, dtype, "state", stored_bf16=False)
 
 
 def test_prefill_then_decode_equals_longer_prefill(oracle_mod):
@@ -146,7 +146,7 @@ def test_prefill_then_decode_equals_longer_prefill(oracle_mod):
     torch.cuda.synchronize()
     ro, rS = oracle_mod.fwd(q, k, v, s)
     assert_close(to_host(o), ro[:, :, N], "bf16", "o")
-    assert_close(to_host(S), rS, "bf16", "S")
+    assert_close(to_host(S), rS, "bf16", "S", stored_bf16=False)
 
 
 BWD_CASES = [
@@ -191,4 +191,4 @@ def test_chunk_length_changes_only_rounding(oracle_mod):
     for C in (32, 64, 128):
         o, S = _run_prefill(q, k, v, s, C, "bf16")
         assert_close(o, ro, "bf16", "o C=%d" % C)
-        assert_close(S, rS, "bf16", "S C=%d" % C)
+        assert_close(S, rS, "bf16", "S C=%d" % C, stored_bf16=False)
