@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Benchmark of the Lightning Attention layer on one MI355X.
+
+One JSON line on stdout.  The headline ("value") is bf16 prefill throughput in
+tokens/s on the 128K-token workload (B=1, H=32, N=131072, d=128, chunk 128):
+one step is one whole la_prefill call (segment pre-pass + main pass) over the
+sequence, inputs resident in HBM.  The same line carries:
+  * "roofline": the main prefill kernel's algorithmic HBM bytes per launch over
+    its HIP-event-timed average duration, against 8 TB/s;
+  * "decode": the batched decode step (B=64, H=32, d=128), 1000 consecutive
+    steps with fresh q/k/v each, microseconds per step and HBM fraction;
+  * "train": forward + backward at B=4, H=16, N=32768, d=128, chunk 64;
+  * "cpu_baseline": the fp64 CPU oracle on a bounded sample of the headline
+    workload (the first tokens of all 32 heads), on the host's cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix, TFLOP/s
+METRIC = "Lightning-attn prefill tokens/s at 128K; decode-step μs; % of MFMA/HBM peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_counts(B, H, N, d, C):
+    """Algorithmic bytes and flops of one forward pass (q, k, v read, o
+    written, final state written; causal intra-chunk products counted once)."""
+    bytes_ = 4 * B * H * N * d * 2 + B * H * d * d * 4
+    flops = B * H * N * (2 * (C + 1) * d + 4 * d * d)
+    return bytes_, flops
+
+
+def prefill_mfma_executed(B, H, N, d, C):
+    """Matrix-core flops the bf16 kernel issues: causal 16x16 score tiles, and
+    hi+lo passes for P.V, S.Q and K^T.(bV)."""
+    nqb, ksd, ksc, nt = C // 16, d // 32, C // 32, d // 16
+    tiles = nqb * (nqb + 1) // 2 * ksd
+    pv = nt * sum(qb // 2 + 1 for qb in range(nqb)) * 2
+    inter = nt * nqb * ksd * 2
+    state = nt * nt * ksc * 2
+    chunks = B * H * ((N + C - 1) // C)
+    return chunks * (tiles + pv + inter + state) * 16 * 16 * 32 * 2
+
+
+def bench_prefill(args, torch, la, la_inputs):
+    B, H, N, d, C = 1, 32, 131072, 128, 128
+    dev = torch.device("cuda:0")
+    q, k, v = la_inputs.qkv_device(2, B, H, N, d, dev, torch.bfloat16)
+    slope = torch.from_numpy(la_inputs.slopes(H)).to(dev)
+    o = torch.empty_like(q)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    nws = la.workspace_bytes(0, la.LA_BF16, B, H, N, d, C)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(e0=None, e1=None, e2=None):
+        if e0 is not None:
+            e0.record(stream)
+        la.prefill_prepass(k, v, slope, C, ws, stream=stream)
+        if e1 is not None:
+            e1.record(stream)
+        la.prefill_main(q, k, v, slope, C, ws, o, state_out=S, stream=stream)
+        if e2 is not None:
+            e2.record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(*ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = ev[0][0].elapsed_time(ev[-1][2])
+    main_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    ms_per_step = total_ms / args.steps
+    bytes_, flops = prefill_counts(B, H, N, d, C)
+    achieved = bytes_ / (main_ms * 1e-3) / 1e9
+    res = {
+        "B": B, "H": H, "N": N, "d": d, "C": C,
+        "ms_per_step": ms_per_step,
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+        "tokens_per_s": B * N / (ms_per_step * 1e-3),
+        "main_kernel_ms": main_ms,
+        "prepass_ms": pre_ms,
+        "roofline": {
+            "kernel": "fwd_bf16_kernel<128,128> (la_prefill_main)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "bytes_per_launch": bytes_,
+        },
+        "mfma": {
+            "algorithmic_tflops": flops / (main_ms * 1e-3) / 1e12,
+            "algorithmic_frac": flops / (main_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFS,
+            "executed_tflops": prefill_mfma_executed(B, H, N, d, C) / (main_ms * 1e-3) / 1e12,
+            "executed_frac": prefill_mfma_executed(B, H, N, d, C) / (main_ms * 1e-3) / 1e12
+            / BF16_MFMA_PEAK_TFS,
+            "peak_tflops": BF16_MFMA_PEAK_TFS,
+        },
+        "workspace_bytes": nws,
+    }
+    del q, k, v, o, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(args, torch, la, la_inputs):
+    B, H, d, steps = 64, 32, 128, args.decode_steps
+    dev = torch.device("cuda:0")
+    slope = torch.from_numpy(la_inputs.slopes(H)).to(dev)
+    S0 = torch.from_numpy(la_inputs.decode_state(3, B, H, d)).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    scale = 1.0 / d ** 0.5
+    qs, ks, vs = (
+        (torch.randn((steps, B, H, d), generator=g, device=dev) * scale).to(torch.bfloat16)
+        for _ in range(3)
+    )
+    o = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
+    S = S0.clone()
+    stream = torch.cuda.current_stream()
+    for i in range(min(10, steps)):
+        la.decode_step(qs[i], ks[i], vs[i], slope, S, out=o, stream=stream)
+    S.copy_(S0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        la.decode_step(qs[i], ks[i], vs[i], slope, S, out=o, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    bytes_ = 2 * B * H * d * d * 4 + 4 * B * H * d * 2
+    achieved = bytes_ / (us * 1e-6) / 1e9
+    res = {
+        "B": B, "H": H, "d": d, "steps": steps,
+        "us_per_step": us,
+        "tokens_per_s": B / (us * 1e-6),
+        "roofline": {"kernel": "decode_kernel<128>", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "bytes_per_launch": bytes_},
+        "note": "the 134 MB state fits the 256 MB Infinity Cache, so repeated steps can "
+                "exceed the HBM rate",
+    }
+    del qs, ks, vs, S, S0
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_train(args, torch, la, la_inputs):
+    B, H, N, d, C = 4, 16, 32768, 128, 64
+    dev = torch.device("cuda:0")
+    q, k, v = la_inputs.qkv_device(4, B, H, N, d, dev, torch.bfloat16)
+    dout = la_inputs.upstream_grad_device(4, B, H, N, d, dev, torch.bfloat16)
+    slope = torch.from_numpy(la_inputs.slopes(H)).to(dev)
+    o = torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    nws = max(la.workspace_bytes(0, la.LA_BF16, B, H, N, d, C),
+              la.workspace_bytes(1, la.LA_BF16, B, H, N, d, C))
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    steps = max(2, args.train_steps)
+
+    def step(e=None):
+        if e is not None:
+            e[0].record(stream)
+        la.prefill(q, k, v, slope, chunk=C, out=o, return_state=False, workspace=ws, stream=stream)
+        if e is not None:
+            e[1].record(stream)
+        la.prefill_bwd(q, k, v, dout, slope, chunk=C, dq=dq, dk=dk, dv=dv, workspace=ws,
+                       stream=stream)
+        if e is not None:
+            e[2].record(stream)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    fb, _ = prefill_counts(B, H, N, d, C)
+    bb = 7 * B * H * N * d * 2
+    res = {
+        "B": B, "H": H, "N": N, "d": d, "C": C,
+        "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+        "tokens_per_s": B * N / ((fwd_ms + bwd_ms) * 1e-3),
+        "fwd_hbm_frac": fb / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "bwd_hbm_frac": bb / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "bwd_bytes_note": "7 tensors of B*H*N*d bf16 (q, k, v, dout read; dq, dk, dv written)",
+    }
+    del q, k, v, dout, o, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(args, la_inputs):
+    """The fp64 oracle on the first tokens of the 128K workload (all 32 heads),
+    in pieces of 4096 tokens carried through the state, until about
+    args.cpu_seconds of oracle time have passed."""
+    import oracle
+
+    oracle.build()
+    B, H, d, piece = 1, 32, 128, 4096
+    s = la_inputs.slopes(H)
+    S = None
+    done, spent = 0, 0.0
+    while spent < args.cpu_seconds and done < 131072:
+        q, k, v = la_inputs.qkv(2, B, H, piece, d, dtype="bf16", step=done // piece)
+        t0 = time.perf_counter()
+        _, S = oracle.fwd(q, k, v, s, S)
+        spent += time.perf_counter() - t0
+        done += piece
+    return {
+        "value": done / spent,
+        "unit": "tokens/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "fp64 recurrent oracle, first %d tokens of the B=1 H=32 d=128 prefill "
+                  "(all 32 heads, bf16-valued inputs), %.1f s" % (done, spent),
+    }
+
+
+def copy_calibration(torch):
+    """A plain 1 GiB device-to-device copy, for scaling HBM counters."""
+    dev = torch.device("cuda:0")
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log("copy calibration: 1 GiB copied (read 1 GiB, write 1 GiB)")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--train-steps", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "train"], default=None,
+                    help="run one workload only (profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU; --gpus %d (WORLD_SIZE %d) is not "
+              "supported -- sharding is described in DESIGN.md, not built" % (args.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import hybrid_linear_attention_lightning_amd as la
+    import la_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    la.lib()
+    if args.copy_calibration:
+        copy_calibration(torch)
+    out = {}
+    if args.only in (None, "prefill"):
+        log("prefill 128K ...")
+        out["prefill"] = bench_prefill(args, torch, la, la_inputs)
+        log("  %.3f ms/step" % out["prefill"]["ms_per_step"])
+    if args.only in (None, "decode"):
+        log("decode B=64 ...")
+        out["decode"] = bench_decode(args, torch, la, la_inputs)
+        log("  %.2f us/step" % out["decode"]["us_per_step"])
+    if args.only in (None, "train"):
+        log("train fwd+bwd B=4 H=16 N=32K ...")
+        out["train"] = bench_train(args, torch, la, la_inputs)
+        log("  fwd %.3f ms, bwd %.3f ms" % (out["train"]["fwd_ms"], out["train"]["bwd_ms"]))
+    cpu = None
+    if not args.no_cpu_baseline and args.only in (None, "prefill"):
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(args, la_inputs)
+        log("  %.1f tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
+
+    p = out.get("prefill")
+    line = {
+        "metric": METRIC,
+        "value": p["tokens_per_s"] if p else None,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": p["ms_per_step"] if p else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: q,k,v ~ N(0,1)/sqrt(d) bf16, slopes 2^(-8(h+1)/H), torch seeded generator",
+        "config": {"workload": "lightning-attention prefill, bf16, B=1 H=32 N=131072 d=128 chunk=128",
+                   "B": 1, "H": 32, "N": 131072, "d": 128, "C": 128},
+        "roofline": p["roofline"] if p else None,
+        "cpu_baseline": cpu,
+        "prefill": p,
+        "decode": out.get("decode"),
+        "train": out.get("train"),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

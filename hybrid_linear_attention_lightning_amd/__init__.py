@@ -41,6 +41,8 @@ STATUS = {
 _P, _I, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 SIGNATURES = {
     "la_prefill": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "la_prefill_prepass": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
+    "la_prefill_main": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "la_decode_step": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "la_prefill_bwd": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "la_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
@@ -146,6 +148,42 @@ def prefill(q, k, v, slope, chunk=64, state_in=None, out=None, state_out=None,
     )
     _check("la_prefill", code)
     return out, state_out
+
+
+def prefill_prepass(k, v, slope, chunk, workspace, state_in=None, stream=None):
+    """First half of `prefill`: segment start states into `workspace`
+    (a uint8 cuda tensor of at least workspace_bytes(0, ...) bytes)."""
+    B, H, N, d = k.shape
+    dt = _dtype_code(k)
+    nbytes = workspace_bytes(0, dt, B, H, N, d, chunk)
+    code = lib().la_prefill_prepass(
+        dt, B, H, N, d, chunk, _dev(k, "k"), _dev(v, "v", k.dtype),
+        _dev(slope, "slope", torch.float32),
+        None if state_in is None else _dev(state_in, "state_in", torch.float32),
+        None if nbytes == 0 else _dev(workspace, "workspace"),
+        0 if nbytes == 0 else workspace.numel() * workspace.element_size(), _stream(stream),
+    )
+    _check("la_prefill_prepass", code)
+
+
+def prefill_main(q, k, v, slope, chunk, workspace, out, state_out=None, state_in=None,
+                 stream=None):
+    """Second half of `prefill`: all segments from the states prefill_prepass
+    left in `workspace`."""
+    B, H, N, d = q.shape
+    dt = _dtype_code(q)
+    nbytes = workspace_bytes(0, dt, B, H, N, d, chunk)
+    code = lib().la_prefill_main(
+        dt, B, H, N, d, chunk, _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+        _dev(slope, "slope", torch.float32),
+        None if state_in is None else _dev(state_in, "state_in", torch.float32),
+        _dev(out, "out", q.dtype),
+        None if state_out is None else _dev(state_out, "state_out", torch.float32),
+        None if nbytes == 0 else _dev(workspace, "workspace"),
+        0 if nbytes == 0 else workspace.numel() * workspace.element_size(), _stream(stream),
+    )
+    _check("la_prefill_main", code)
+    return out
 
 
 def decode_step(q, k, v, slope, state, out=None, stream=None):

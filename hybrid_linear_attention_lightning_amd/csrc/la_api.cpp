@@ -75,11 +75,9 @@ la_status_t check_seq(la_dtype_t dt, int B, int H, int N, int d, int C) {
   return LA_OK;
 }
 
-// One causal (or, with reverse, anti-causal) pass with its segment pre-pass.
-la_status_t run_pass(la_dtype_t dt, const Plan& pl, int B, int H, int N, int d, int C,
-                     const void* q, const void* k, const void* v, const float* slope,
-                     const float* state_in, void* o, float* state_out, bool reverse,
-                     void* workspace, hipStream_t s) {
+la::FwdPass make_fwd(const Plan& pl, int B, int H, int N, int d, int C, const void* q,
+                     const void* k, const void* v, const float* slope, const float* state_in,
+                     void* o, float* state_out, bool reverse, void* workspace) {
   la::FwdPass fp{};
   fp.q = q;
   fp.k = k;
@@ -96,45 +94,93 @@ la_status_t run_pass(la_dtype_t dt, const Plan& pl, int B, int H, int N, int d, 
   fp.reverse = reverse;
   fp.seg_len = pl.seg_len;
   fp.nseg = pl.nseg;
+  if (pl.nseg > 1) fp.seg_states = (const float*)((const char*)workspace + pl.pieces_bytes);
+  return fp;
+}
+
+// Segment start states (piece kernel + scan); nothing when there is one segment.
+la_status_t run_prepass(const Plan& pl, int B, int H, int N, int d, int C, const void* k,
+                        const void* v, const float* slope, const float* state_in, bool reverse,
+                        void* workspace, hipStream_t s) {
+  if (pl.nseg <= 1) return LA_OK;
+  float* pieces = (float*)workspace;
+  float* seg_states = (float*)((char*)workspace + pl.pieces_bytes);
+  la::PiecePass pp{};
+  pp.k = k;
+  pp.v = v;
+  pp.slope = slope;
+  pp.pieces = pieces;
+  pp.B = B;
+  pp.H = H;
+  pp.N = N;
+  pp.D = d;
+  pp.C = C;
+  pp.reverse = reverse;
+  pp.piece_len = pl.piece_len;
+  pp.npiece = pl.npiece;
+  pp.seg_len = pl.seg_len;
+  pp.nseg = pl.nseg;
+  la_status_t st = hip_status(la::launch_pieces_bf16(pp, s));
+  if (st != LA_OK) return st;
+  la::ScanPass sp{};
+  sp.pieces = pieces;
+  sp.state_in = state_in;
+  sp.seg_states = seg_states;
+  sp.slope = slope;
+  sp.B = B;
+  sp.H = H;
+  sp.N = N;
+  sp.D = d;
+  sp.piece_len = pl.piece_len;
+  sp.npiece = pl.npiece;
+  sp.seg_len = pl.seg_len;
+  sp.nseg = pl.nseg;
+  return hip_status(la::launch_scan(sp, s));
+}
+
+la_status_t run_main(la_dtype_t dt, const la::FwdPass& fp, hipStream_t s) {
   if (dt == LA_F32) return hip_status(la::launch_fwd_f32(fp, s));
-  if (pl.nseg > 1) {
-    float* pieces = (float*)workspace;
-    float* seg_states = (float*)((char*)workspace + pl.pieces_bytes);
-    la::PiecePass pp{};
-    pp.k = k;
-    pp.v = v;
-    pp.slope = slope;
-    pp.pieces = pieces;
-    pp.B = B;
-    pp.H = H;
-    pp.N = N;
-    pp.D = d;
-    pp.C = C;
-    pp.reverse = reverse;
-    pp.piece_len = pl.piece_len;
-    pp.npiece = pl.npiece;
-    pp.seg_len = pl.seg_len;
-    pp.nseg = pl.nseg;
-    la_status_t st = hip_status(la::launch_pieces_bf16(pp, s));
-    if (st != LA_OK) return st;
-    la::ScanPass sp{};
-    sp.pieces = pieces;
-    sp.state_in = state_in;
-    sp.seg_states = seg_states;
-    sp.slope = slope;
-    sp.B = B;
-    sp.H = H;
-    sp.N = N;
-    sp.D = d;
-    sp.piece_len = pl.piece_len;
-    sp.npiece = pl.npiece;
-    sp.seg_len = pl.seg_len;
-    sp.nseg = pl.nseg;
-    st = hip_status(la::launch_scan(sp, s));
-    if (st != LA_OK) return st;
-    fp.seg_states = seg_states;
-  }
   return hip_status(la::launch_fwd_bf16(fp, s));
+}
+
+// One causal (or, with reverse, anti-causal) pass with its segment pre-pass.
+la_status_t run_pass(la_dtype_t dt, const Plan& pl, int B, int H, int N, int d, int C,
+                     const void* q, const void* k, const void* v, const float* slope,
+                     const float* state_in, void* o, float* state_out, bool reverse,
+                     void* workspace, hipStream_t s) {
+  la_status_t st = run_prepass(pl, B, H, N, d, C, k, v, slope, state_in, reverse, workspace, s);
+  if (st != LA_OK) return st;
+  return run_main(dt, make_fwd(pl, B, H, N, d, C, q, k, v, slope, state_in, o, state_out,
+                               reverse, workspace),
+                  s);
+}
+
+// Checks of la_prefill / la_prefill_main (q and o may be null for the prepass).
+la_status_t check_prefill(la_dtype_t dt, int B, int H, int N, int d, int C, const void* q,
+                          const void* k, const void* v, const float* slope,
+                          const float* state_in, const void* o, const float* state_out,
+                          const void* workspace, size_t workspace_bytes, bool need_qo,
+                          Plan* plan) {
+  la_status_t st = check_seq(dt, B, H, N, d, C);
+  if (st != LA_OK) return st;
+  if (!k || !v || !slope || (need_qo && (!q || !o))) return LA_ERR_NULL_POINTER;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state_in) ||
+      !aligned16(state_out) || ((uintptr_t)slope & 3u))
+    return LA_ERR_ALIGNMENT;
+  const size_t esz = dt == LA_BF16 ? 2 : 4;
+  const size_t tb = (size_t)B * H * N * d * esz;
+  const size_t sb = (size_t)B * H * d * d * sizeof(float);
+  if (o && (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb)))
+    return LA_ERR_ALIAS;
+  if (state_in && state_out && state_in != state_out && overlap(state_in, sb, state_out, sb))
+    return LA_ERR_ALIAS;
+  if (state_out && ((q && overlap(state_out, sb, q, tb)) || overlap(state_out, sb, k, tb) ||
+                    overlap(state_out, sb, v, tb) || (o && overlap(state_out, sb, o, tb))))
+    return LA_ERR_ALIAS;
+  *plan = make_plan(dt, B, H, N, d, C);
+  if (plan->ws() > 0 && (!workspace || workspace_bytes < plan->ws())) return LA_ERR_WORKSPACE;
+  if (plan->ws() > 0 && !aligned16(workspace)) return LA_ERR_ALIGNMENT;
+  return LA_OK;
 }
 
 }  // namespace
@@ -146,27 +192,45 @@ la_status_t la_prefill(la_dtype_t dt, int B, int H, int N, int d, int C, const v
                        void* o, float* state_out, void* workspace, size_t workspace_bytes,
                        void* stream) {
   try {
-    la_status_t st = check_seq(dt, B, H, N, d, C);
+    Plan pl;
+    const la_status_t st = check_prefill(dt, B, H, N, d, C, q, k, v, slope, state_in, o,
+                                         state_out, workspace, workspace_bytes, true, &pl);
     if (st != LA_OK) return st;
-    if (!q || !k || !v || !slope || !o) return LA_ERR_NULL_POINTER;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-        !aligned16(state_in) || !aligned16(state_out) || ((uintptr_t)slope & 3u))
-      return LA_ERR_ALIGNMENT;
-    const size_t esz = dt == LA_BF16 ? 2 : 4;
-    const size_t tb = (size_t)B * H * N * d * esz;
-    const size_t sb = (size_t)B * H * d * d * sizeof(float);
-    if (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb))
-      return LA_ERR_ALIAS;
-    if (state_in && state_out && state_in != state_out && overlap(state_in, sb, state_out, sb))
-      return LA_ERR_ALIAS;
-    if (state_out && (overlap(state_out, sb, q, tb) || overlap(state_out, sb, k, tb) ||
-                      overlap(state_out, sb, v, tb) || overlap(state_out, sb, o, tb)))
-      return LA_ERR_ALIAS;
-    const Plan pl = make_plan(dt, B, H, N, d, C);
-    if (pl.ws() > 0 && (!workspace || workspace_bytes < pl.ws())) return LA_ERR_WORKSPACE;
-    if (pl.ws() > 0 && !aligned16(workspace)) return LA_ERR_ALIGNMENT;
     return run_pass(dt, pl, B, H, N, d, C, q, k, v, slope, state_in, o, state_out, false,
                     workspace, (hipStream_t)stream);
+  } catch (...) {
+    return LA_ERR_HIP;
+  }
+}
+
+la_status_t la_prefill_prepass(la_dtype_t dt, int B, int H, int N, int d, int C, const void* k,
+                               const void* v, const float* slope, const float* state_in,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    Plan pl;
+    const la_status_t st = check_prefill(dt, B, H, N, d, C, nullptr, k, v, slope, state_in,
+                                         nullptr, nullptr, workspace, workspace_bytes, false, &pl);
+    if (st != LA_OK) return st;
+    return run_prepass(pl, B, H, N, d, C, k, v, slope, state_in, false, workspace,
+                       (hipStream_t)stream);
+  } catch (...) {
+    return LA_ERR_HIP;
+  }
+}
+
+la_status_t la_prefill_main(la_dtype_t dt, int B, int H, int N, int d, int C, const void* q,
+                            const void* k, const void* v, const float* slope,
+                            const float* state_in, void* o, float* state_out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  try {
+    Plan pl;
+    const la_status_t st = check_prefill(dt, B, H, N, d, C, q, k, v, slope, state_in, o,
+                                         state_out, workspace, workspace_bytes, true, &pl);
+    if (st != LA_OK) return st;
+    return run_main(dt,
+                    make_fwd(pl, B, H, N, d, C, q, k, v, slope, state_in, o, state_out, false,
+                             workspace),
+                    (hipStream_t)stream);
   } catch (...) {
     return LA_ERR_HIP;
   }

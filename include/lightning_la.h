@@ -76,7 +76,9 @@ typedef enum {
  *
  *   dt        LA_F32 or LA_BF16 (type of q, k, v, o)
  *   B, H, N   >= 1;  d in {64, 128} (LA_F32 also allows 16 and 32)
- *   C         chunk length in {16, 32, 64, 128}; N need not be a multiple of C
+ *   C         chunk length: {16, 32, 64, 128} for LA_F32, {32, 64, 128} for
+ *             LA_BF16 (16 gives LA_ERR_UNSUPPORTED); N need not be a multiple
+ *             of C.  B*H*N above 2^30 gives LA_ERR_UNSUPPORTED.
  *   q, k, v   [B][H][N][d] of dt, 16-byte aligned
  *   slope     [H] fp32, the decay is exp(-slope[h]); any finite slope >= 0
  *   state_in  [B][H][d][d] fp32, or NULL for a zero initial state
@@ -91,6 +93,34 @@ la_status_t la_prefill(la_dtype_t dt, int B, int H, int N, int d, int C,
                        const float *slope, const float *state_in, void *o,
                        float *state_out, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ *
+ * la_prefill_prepass / la_prefill_main -- la_prefill in two calls.
+ *
+ * When B*H is small, la_prefill cuts each sequence into segments that run in
+ * parallel.  la_prefill_prepass computes the state entering every segment
+ * from K, V and state_in -- per-piece local states combined by decay, the
+ * "local recursion + global correction" of the context-parallel scheme on the
+ * "Context Parallel for Lightning Attention" section -- and leaves them in
+ * `workspace`.  la_prefill_main then runs all segments from those states.
+ * la_prefill is exactly la_prefill_prepass followed by la_prefill_main on the
+ * same stream; the split lets a caller time or overlap the two parts.
+ *
+ * Both calls take the arguments of la_prefill (the prepass only the ones it
+ * reads) and must see the same dt, B, H, N, d, C, k, v, slope, state_in and
+ * workspace; the workspace must not be modified between the two calls.  When
+ * la_workspace_bytes(0, ...) is 0 the prepass enqueues nothing.
+ * ------------------------------------------------------------------------ */
+la_status_t la_prefill_prepass(la_dtype_t dt, int B, int H, int N, int d, int C,
+                               const void *k, const void *v,
+                               const float *slope, const float *state_in,
+                               void *workspace, size_t workspace_bytes,
+                               void *stream);
+la_status_t la_prefill_main(la_dtype_t dt, int B, int H, int N, int d, int C,
+                            const void *q, const void *k, const void *v,
+                            const float *slope, const float *state_in, void *o,
+                            float *state_out, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------ *
  * la_decode_step -- one generated token per (b, h), on a carried state.
