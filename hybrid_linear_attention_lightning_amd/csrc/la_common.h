@@ -57,6 +57,29 @@ __device__ __forceinline__ u32x2_t lds_read8(const uint16_t* p) {
   return *reinterpret_cast<const u32x2_t*>(p);
 }
 
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives element (i % 4) of the 8-byte rows addressed by
+// lanes 4r + i/4, for r = 0..3.  If lane i of a group points at row k0 + i/4,
+// columns c0 + 4 (i % 4) .. +3 of a row-major bf16 tile, lane i receives the
+// column c0 + i of rows k0 .. k0+3: a column fragment of a row-major tile.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2_t lds_read_tr8(const uint16_t* p) {
+  const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, r);
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its outstanding global loads (which may be prefetching
+// the next chunk, directly into LDS or into registers).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 2^x without the denormal-range fix-up of exp2f (v_exp_f32; results below
+// 2^-126 flush to zero, which the decay factors tolerate).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Split four fp32 values into bf16 hi + lo parts (x ~= hi + lo to about 2^-16
 // relative): the matrix cores then see 16 significant bits instead of 8.
 __device__ __forceinline__ void split4(f32x4_t x, u32x2_t& hi, u32x2_t& lo) {

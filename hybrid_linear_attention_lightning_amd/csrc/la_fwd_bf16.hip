@@ -23,10 +23,12 @@
 //    S and b*V -- are handed to the matrix cores as bf16 hi + lo pairs, so the
 //    products carry ~16 significant bits (plain bf16 operands would lose as
 //    much accuracy as the final rounding of the output);
-//  * Q and K are staged row-major in LDS, K and V also transposed (feature
-//    rows) in "fragment order" (frag_pos), so MFMA results feed back as MFMA
-//    operands without a transpose; the masked scores of a chunk are exchanged
-//    through LDS in the region of K and K^T, which are dead by then.
+//  * Q, K and V are staged row-major in LDS with an XOR swizzle of 16-byte
+//    chunks that keeps every access pattern below free of bank conflicts;
+//    K^T and V^T fragments (contractions over tokens) come straight from the
+//    row-major tiles through the transposing LDS read of gfx950; the masked
+//    scores of a chunk are exchanged between waves through LDS in the exact
+//    register order of the MFMA B operand.
 // The same kernel in STATE_ONLY mode computes piece states (K^T diag(b) V
 // accumulated over a piece) for the segment pre-pass.
 #include "la_common.h"
@@ -49,30 +51,38 @@ struct Cfg {
   static constexpr int KSD = D / 32;   // 32-feature contraction steps
   static constexpr int NT = D / 16;    // 16-feature tiles (key and value side)
   static constexpr int WT = NT / 4;    // value tiles owned by each wave
-  static constexpr int QS = D + 8;     // row stride (elements) of Qs / Ks
-  static constexpr int TS = C + 8;     // row stride (elements) of Kt / Vt
   static constexpr int NFRAG = frag_base(NQB);
-  static constexpr int MAXT = NQB == 8 ? 9 : NQB == 4 ? 4 : 2;  // P^T tiles per wave
-  static constexpr int QCH = STATE_ONLY ? 0 : (C * D / 8 + kThreads - 1) / kThreads;
-  static constexpr int NB = C * D / 64;  // 8x8 blocks per tensor
-  static constexpr int KVB = (2 * NB + kThreads - 1) / kThreads;
-  static constexpr int Q_ELEMS = STATE_ONLY ? 0 : C * QS;
-  static constexpr int K_ELEMS = STATE_ONLY ? 0 : C * QS;
-  static constexpr int T_ELEMS = D * TS;
-  static constexpr int PT_HALF = NFRAG * 64 * 8;  // one of P_hi / P_lo
-  // the P^T exchange reuses the space of K and K^T when it fits there
-  static constexpr bool PT_ALIAS = STATE_ONLY || 2 * PT_HALF <= K_ELEMS + T_ELEMS;
-  static constexpr int LDS_ELEMS = Q_ELEMS + K_ELEMS + 2 * T_ELEMS + (PT_ALIAS ? 0 : 2 * PT_HALF);
+  static constexpr int CH = C * D / 8;  // 16-byte chunks per tile
+  static constexpr int QCH = (CH + kThreads - 1) / kThreads;  // per thread and tensor
+  static constexpr int NTEN = STATE_ONLY ? 4 : 3;  // K,V double-buffered / K,V,Q
+  static constexpr int TILE = C * D;                            // elements per tile
+  static constexpr int PT_HALF = NFRAG * 64 * 8;                // one of P_hi / P_lo
+  static constexpr int LDS_ELEMS = NTEN * TILE + (STATE_ONLY ? 0 : 2 * PT_HALF);
   static_assert(C == 32 || C == 64 || C == 128, "chunk");
   static_assert(D == 64 || D == 128, "head dim");
 };
 
-// (key block, query block) of the m-th P^T tile of a wave; balanced so that
-// every wave does the same number of 16x16 tiles when C = 128.
+// Element offset of (row, col) in a swizzled row-major [C][D] bf16 tile: the
+// 16-byte chunk index is XORed with a function of the row chosen so that the
+// row-fragment reads (16 rows x 16 B), the permuted 8-byte Q reads, the
+// transposing reads (4 rows x 32 B per lane group) and the staging writes are
+// all free of LDS bank conflicts.
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+  int s;
+  if constexpr (D == 128)
+    s = ((row & 3) << 2) | ((row >> 2) & 3);
+  else
+    s = (((row & 3) << 1) ^ (row >> 2)) & 7;
+  return row * D + ((((col >> 3) ^ s) & (D / 8 - 1)) << 3) + (col & 7);
+}
+
+// (key block, query block) of the m-th P^T tile of a wave.  For C = 128 wave w
+// takes query blocks 7-w and w (9 tiles each wave); otherwise query block w.
 template <int NQB>
 __device__ __forceinline__ bool tile_of(int wave, int m, int& kb, int& qb) {
   if constexpr (NQB == 8) {
-    const int first = 8 - wave;  // tiles of query block 7-wave
+    const int first = 8 - wave;
     if (m < first) {
       kb = m;
       qb = 7 - wave;
@@ -91,13 +101,12 @@ __device__ __forceinline__ bool tile_of(int wave, int m, int& kb, int& qb) {
 template <int C, int D, bool STATE_ONLY>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdPass p, PiecePass pp) {
   using G = Cfg<C, D, STATE_ONLY>;
+  constexpr int MAXT = G::NQB == 8 ? 9 : G::NQB == 4 ? 4 : 2;
   __shared__ __attribute__((aligned(16))) uint16_t smem[G::LDS_ELEMS];
-  uint16_t* Qs = smem;
-  uint16_t* Ks = Qs + G::Q_ELEMS;
-  uint16_t* Kt = Ks + G::K_ELEMS;
-  uint16_t* Vt = Kt + G::T_ELEMS;
-  // P^T hi / lo fragments, written after K and K^T are dead
-  uint16_t* Pth = G::PT_ALIAS ? Ks : Vt + G::T_ELEMS;
+  uint16_t* Ks = smem;
+  uint16_t* Vs = Ks + G::TILE;
+  uint16_t* Qs = Vs + G::TILE;  // without STATE_ONLY (STATE_ONLY: second K,V buffer)
+  uint16_t* Pth = Qs + G::TILE;
   uint16_t* Ptl = Pth + G::PT_HALF;
 
   const int tid = threadIdx.x;
@@ -162,20 +171,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdPass p, PieceP
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int e = li - 4 * lg - r;
-    md[r] = e >= 0 ? exp2f(-sl2 * (float)e) : 0.f;
-    mo[r] = exp2f(-sl2 * (float)(16 + e));
+    md[r] = e >= 0 ? fast_exp2(-sl2 * (float)e) : 0.f;
+    mo[r] = fast_exp2(-sl2 * (float)(16 + e));
   }
-  float aq[G::NQB];  // a_i for this lane's query column in each query block
-#pragma unroll
-  for (int qb = 0; qb < G::NQB; ++qb) aq[qb] = exp2f(-sl2 * (float)(16 * qb + li + 1));
-  // Full chunk: b for the e-th token of a V fragment of step ks (token
-  // 32ks + xl(e)) is lambda^(32 (KSC-1-ks)) * bl[e] with bl[e] = lambda^(31 - xl(e)).
+  // Full chunk: b for token 32ks + 8lg + e of a fragment is
+  // lambda^(32 (KSC-1-ks)) * bl[e] with bl[e] = lambda^(31 - 8lg - e).
   float bl[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int xl = e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4;
-    bl[e] = exp2f(-sl2 * (float)(31 - xl));
-  }
+  for (int e = 0; e < 8; ++e) bl[e] = fast_exp2(-sl2 * (float)(31 - 8 * lg - e));
 
   // ---- fp32 state: this wave's WT value tiles x NT key tiles ------------
   // S[wt][t][r] = S[key 16t + 4lg + r][value 16(wave*WT + wt) + li]
@@ -190,145 +193,59 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdPass p, PieceP
         S[wt][t][r] = s_init ? s_init[(size_t)(16 * t + 4 * lg + r) * D + col] : 0.f;
     }
 
-  // ---- staging registers ------------------------------------------------
-  u32x4_t qr[G::QCH > 0 ? G::QCH : 1];
-  u32x4_t kvr[G::KVB][8];
+  // ---- staging ------------------------------------------------------------
+  // K and V go global -> LDS directly (no registers), each into a tile that
+  // is dead by the time the load is issued; Q goes global -> registers one
+  // chunk ahead -> swizzled LDS at the top of the next chunk.  Rows past the
+  // end of the sequence read the last valid row: such K and V rows only ever
+  // meet zero weights (causal mask, b = 0), and Q rows past the end produce
+  // outputs that are not stored.
   auto tok = [&](int tau) { return reverse ? (N - 1 - tau) : tau; };
-
-  auto load_chunk = [&](int tc, int n) {
-    if constexpr (!STATE_ONLY) {
+  constexpr int RPI = 64 / (D / 8);  // rows per wave-wide 16-byte-per-lane load
+  auto load_direct = [&](const uint16_t* src, uint16_t* tile, int tc, int n) {
 #pragma unroll
-      for (int m = 0; m < G::QCH; ++m) {
-        const int id = tid + kThreads * m;
-        const int row = id / (D / 8), c8 = id % (D / 8);
-        qr[m] = (id < C * D / 8 && row < n)
-                    ? *reinterpret_cast<const u32x4_t*>(qg + (size_t)tok(tc + row) * D + 8 * c8)
-                    : u32x4_t{0, 0, 0, 0};
-      }
+    for (int j = wave; j < C / RPI; j += 4) {
+      const int row = RPI * j + lane / (D / 8);
+      // lane l lands in physical chunk l % (D/8) of its row: fetch the logical
+      // chunk the swizzle maps there (XOR is its own inverse)
+      const int c = swz<D>(row, 8 * (lane % (D / 8))) - row * D;
+      const uint16_t* g = src + (size_t)tok(tc + min(row, n - 1)) * D + c;
+      __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(tile + RPI * j * D),
+                                       16, 0, 0);
     }
+  };
+  u32x4_t qstg[G::QCH];
+  auto load_q = [&](int tc, int n) {
 #pragma unroll
-    for (int m = 0; m < G::KVB; ++m) {
-      const int blk = tid + kThreads * m;
-      const bool isk = blk < G::NB;
-      const int bid = isk ? blk : blk - G::NB;
-      const int cg = bid % (D / 8), tg = bid / (D / 8);
-      const int tb = tg >> 2, g = tg & 3;
-      const uint16_t* src = isk ? kg : vg;
+    for (int m = 0; m < G::QCH; ++m) {
+      const int id = tid + kThreads * m;
+      const int row = id / (D / 8), c8 = id % (D / 8);
+      const size_t off = (size_t)tok(tc + min(row, n - 1)) * D + 8 * c8;
+      if (id < G::CH) qstg[m] = *reinterpret_cast<const u32x4_t*>(qg + off);
+    }
+  };
+  auto store_q = [&]() {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int x = 32 * tb + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4);
-        kvr[m][e] = (blk < 2 * G::NB && x < n)
-                        ? *reinterpret_cast<const u32x4_t*>(src + (size_t)tok(tc + x) * D + 8 * cg)
-                        : u32x4_t{0, 0, 0, 0};
-      }
+    for (int m = 0; m < G::QCH; ++m) {
+      const int id = tid + kThreads * m;
+      if (id < G::CH)
+        *reinterpret_cast<u32x4_t*>(Qs + swz<D>(id / (D / 8), 8 * (id % (D / 8)))) = qstg[m];
     }
   };
 
-  auto store_chunk = [&]() {
-    if constexpr (!STATE_ONLY) {
-#pragma unroll
-      for (int m = 0; m < G::QCH; ++m) {
-        const int id = tid + kThreads * m;
-        if (id < C * D / 8) {
-          const int row = id / (D / 8), c8 = id % (D / 8);
-          *reinterpret_cast<u32x4_t*>(Qs + row * G::QS + 8 * c8) = qr[m];
-        }
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < G::KVB; ++m) {
-      const int blk = tid + kThreads * m;
-      if (blk < 2 * G::NB) {
-        const bool isk = blk < G::NB;
-        const int bid = isk ? blk : blk - G::NB;
-        const int cg = bid % (D / 8), tg = bid / (D / 8);
-        const int tb = tg >> 2, g = tg & 3;
-        if constexpr (!STATE_ONLY) {
-          if (isk) {  // row-major K for Q K^T
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int x = 32 * tb + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4);
-              *reinterpret_cast<u32x4_t*>(Ks + x * G::QS + 8 * cg) = kvr[m][e];
-            }
-          }
-        }
-        // transposed copy: feature row, 8 tokens in fragment order
-        uint16_t* base = (isk ? Kt : Vt) + (8 * cg) * G::TS + 32 * tb + 8 * g;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {  // feature pair (2c, 2c+1)
-          u32x4_t lo, hi;
-#pragma unroll
-          for (int mm = 0; mm < 4; ++mm) {
-            const uint32_t a = kvr[m][2 * mm][c], bb = kvr[m][2 * mm + 1][c];
-            lo[mm] = (a & 0xFFFFu) | (bb << 16);
-            hi[mm] = (a >> 16) | (bb & 0xFFFF0000u);
-          }
-          *reinterpret_cast<u32x4_t*>(base + (2 * c) * G::TS) = lo;
-          *reinterpret_cast<u32x4_t*>(base + (2 * c + 1) * G::TS) = hi;
-        }
-      }
-    }
+  // operand fragment of a column of a row-major tile: 8 consecutive rows
+  // k0..k0+7 (this lane group's 8) at column c0 + li, via two transposing reads
+  auto col_frag = [&](const uint16_t* tile, int k0, int c0) -> u32x4_t {
+    const int row = k0 + (li >> 2), col = c0 + 4 * (li & 3);
+    const u32x2_t a = lds_read_tr8(tile + swz<D>(row, col));
+    const u32x2_t c = lds_read_tr8(tile + swz<D>(row + 4, col));
+    return u32x4_t{a[0], a[1], c[0], c[1]};
   };
 
-  if (tau0 < tau_end) load_chunk(tau0, min(C, tau_end - tau0));
-
-  for (int tc = tau0; tc < tau_end; tc += C) {
-    const int n = min(C, tau_end - tc);
-    store_chunk();
-    __syncthreads();  // chunk tc is in LDS
-    if (tc + C < tau_end) load_chunk(tc + C, min(C, tau_end - tc - C));
-    const float gdec = exp2f(-sl2 * (float)n);
-
-    // S_{c-1} as hi/lo bf16 A-operands of S^T (value row w, 8 keys)
-    u32x4_t sfh[G::WT][G::KSD], sfl[G::WT][G::KSD];
-    // this wave's masked P^T tiles, hi/lo
-    u32x2_t ph[G::MAXT], pl[G::MAXT];
-    if constexpr (!STATE_ONLY) {
-#pragma unroll
-      for (int wt = 0; wt < G::WT; ++wt)
-#pragma unroll
-        for (int ks = 0; ks < G::KSD; ++ks) {
-          u32x2_t h0, l0, h1, l1;
-          split4(S[wt][2 * ks], h0, l0);
-          split4(S[wt][2 * ks + 1], h1, l1);
-          sfh[wt][ks] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
-          sfl[wt][ks] = u32x4_t{l0[0], l0[1], l1[0], l1[1]};
-        }
-
-      // ---- masked scores P^T = (K Q^T) * M^T, kept in registers ----------
-#pragma unroll
-      for (int m = 0; m < G::MAXT; ++m) {
-        int kb, qb;
-        if (!tile_of<G::NQB>(wave, m, kb, qb)) continue;
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < G::KSD; ++ks) {
-          const u32x4_t kf = lds_read16(Ks + (16 * kb + li) * G::QS + 32 * ks + 8 * lg);
-          const u32x4_t qf = lds_read16(Qs + (16 * qb + li) * G::QS + 32 * ks + 8 * lg);
-          acc = mfma16(kf, qf, acc);
-        }
-        const int delta = qb - kb;
-        if (delta == 0) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r] *= md[r];
-        } else {
-          const float f = exp2f(-sl2 * (float)(16 * (delta - 1)));
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r] *= f * mo[r];
-        }
-        split4(acc, ph[m], pl[m]);
-      }
-    }
-
-    // ---- V fragments (row w of V^T, 8 tokens) for this wave's value tiles ----
-    u32x4_t vfr[G::WT][G::KSC];
-#pragma unroll
-    for (int wt = 0; wt < G::WT; ++wt)
-#pragma unroll
-      for (int ks = 0; ks < G::KSC; ++ks)
-        vfr[wt][ks] = lds_read16(Vt + (16 * (wave * G::WT + wt) + li) * G::TS + 32 * ks + 8 * lg);
-
-    // ---- state update S <- lambda^n S + K^T diag(b) V (b*V as hi + lo) ----
+  // S <- lambda^n S + K^T diag(b) V for the chunk in (Kt, Vt); vfr holds this
+  // wave's V^T fragments (value rows, 8 tokens per lane group)
+  auto state_update = [&](const uint16_t* Kt, const u32x4_t (&vfr)[G::WT][G::KSC], int n) {
+    const float gdec = fast_exp2(-sl2 * (float)n);
 #pragma unroll
     for (int wt = 0; wt < G::WT; ++wt)
 #pragma unroll
@@ -339,14 +256,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdPass p, PieceP
     for (int ks = 0; ks < G::KSC; ++ks) {
       float bks[8];
       if (n == C) {
-        const float f = exp2f(-sl2 * (float)(32 * (G::KSC - 1 - ks)));
+        const float f = fast_exp2(-sl2 * (float)(32 * (G::KSC - 1 - ks)));
 #pragma unroll
         for (int e = 0; e < 8; ++e) bks[e] = f * bl[e];
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int x = 32 * ks + (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4);
-          bks[e] = x < n ? exp2f(-sl2 * (float)(n - 1 - x)) : 0.f;
+          const int x = 32 * ks + 8 * lg + e;
+          bks[e] = x < n ? fast_exp2(-sl2 * (float)(n - 1 - x)) : 0.f;
         }
       }
       u32x4_t vbh[G::WT], vbl[G::WT];
@@ -367,75 +284,186 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdPass p, PieceP
       }
 #pragma unroll
       for (int t = 0; t < G::NT; ++t) {
-        const u32x4_t kf = lds_read16(Kt + (16 * t + li) * G::TS + 32 * ks + 8 * lg);
+        const u32x4_t kf = col_frag(Kt, 32 * ks + 8 * lg, 16 * t);
 #pragma unroll
-        for (int wt = 0; wt < G::WT; ++wt) {
-          S[wt][t] = mfma16(kf, vbh[wt], S[wt][t]);
-          S[wt][t] = mfma16(kf, vbl[wt], S[wt][t]);
-        }
+        for (int wt = 0; wt < G::WT; ++wt) S[wt][t] = mfma16(kf, vbh[wt], S[wt][t]);
+#pragma unroll
+        for (int wt = 0; wt < G::WT; ++wt) S[wt][t] = mfma16(kf, vbl[wt], S[wt][t]);
       }
     }
+  };
 
-    if constexpr (!STATE_ONLY) {
-      __syncthreads();  // K and K^T are dead: their space takes the P^T fragments
+  auto load_vfr = [&](const uint16_t* Vt, u32x4_t (&vfr)[G::WT][G::KSC]) {
 #pragma unroll
-      for (int m = 0; m < G::MAXT; ++m) {
+    for (int wt = 0; wt < G::WT; ++wt)
+#pragma unroll
+      for (int ks = 0; ks < G::KSC; ++ks)
+        vfr[wt][ks] = col_frag(Vt, 32 * ks + 8 * lg, 16 * (wave * G::WT + wt));
+  };
+
+  if constexpr (STATE_ONLY) {
+    // K and V double-buffered: chunk c+1 streams in while chunk c is used
+    int buf = 0;
+    if (tau0 < tau_end) {
+      load_direct(kg, Ks, tau0, min(C, tau_end - tau0));
+      load_direct(vg, Vs, tau0, min(C, tau_end - tau0));
+    }
+    for (int tc = tau0; tc < tau_end; tc += C) {
+      const int n = min(C, tau_end - tc);
+      uint16_t* Kc = smem + (2 * buf) * G::TILE;
+      uint16_t* Vc = Kc + G::TILE;
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk tc have landed
+      lds_barrier();
+      if (tc + C < tau_end) {
+        uint16_t* Kn = smem + (2 * (buf ^ 1)) * G::TILE;
+        load_direct(kg, Kn, tc + C, min(C, tau_end - tc - C));
+        load_direct(vg, Kn + G::TILE, tc + C, min(C, tau_end - tc - C));
+      }
+      u32x4_t vfr[G::WT][G::KSC];
+      load_vfr(Vc, vfr);
+      state_update(Kc, vfr, n);
+      lds_barrier();  // chunk tc's tiles are free for chunk tc + 2C
+      buf ^= 1;
+    }
+  } else {
+    if (tau0 < tau_end) {
+      const int n0 = min(C, tau_end - tau0);
+      load_direct(kg, Ks, tau0, n0);
+      load_direct(vg, Vs, tau0, n0);
+      load_q(tau0, n0);
+    }
+    for (int tc = tau0; tc < tau_end; tc += C) {
+      const int n = min(C, tau_end - tc);
+      const bool more = tc + C < tau_end;
+      const int n_next = more ? min(C, tau_end - tc - C) : 0;
+      store_q();
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's K/V loads have landed
+      lds_barrier();                  // chunk tc is in LDS
+      if (more) load_q(tc + C, n_next);
+
+      // ---- masked scores P^T = (K Q^T) * M^T -> LDS as hi/lo B fragments ----
+      // Tile (kb, qb), lane (lg, li) holds keys 16kb + 4lg + r of query
+      // 16qb + li; in the 32-key step kb/2 these are element 4(lg&1) + r of
+      // consumer lane (2(kb&1) + (lg>>1), li).
+#pragma unroll 1
+      for (int m = 0; m < MAXT; ++m) {
         int kb, qb;
         if (!tile_of<G::NQB>(wave, m, kb, qb)) continue;
-        const int off = ((frag_base(qb) + (kb >> 1)) * 64 + lane) * 8;
-        const int half = (kb & 1) * 4;
-        *reinterpret_cast<u32x2_t*>(Pth + off + half) = ph[m];
-        *reinterpret_cast<u32x2_t*>(Ptl + off + half) = pl[m];
-        if (kb == qb && !(qb & 1)) {  // even diagonal: the other half of the step is empty
-          *reinterpret_cast<u32x2_t*>(Pth + off + 4) = u32x2_t{0, 0};
-          *reinterpret_cast<u32x2_t*>(Ptl + off + 4) = u32x2_t{0, 0};
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < G::KSD; ++ks) {
+          const u32x4_t kf = lds_read16(Ks + swz<D>(16 * kb + li, 32 * ks + 8 * lg));
+          const u32x4_t qf = lds_read16(Qs + swz<D>(16 * qb + li, 32 * ks + 8 * lg));
+          acc = mfma16(kf, qf, acc);
+        }
+        const int delta = qb - kb;
+        if (delta == 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[r] *= md[r];
+        } else {
+          const float f = fast_exp2(-sl2 * (float)(16 * (delta - 1)));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[r] *= f * mo[r];
+        }
+        u32x2_t hi, lo;
+        split4(acc, hi, lo);
+        const int base = (frag_base(qb) + (kb >> 1)) * 64;
+        const int off = (base + 16 * (2 * (kb & 1) + (lg >> 1)) + li) * 8 + 4 * (lg & 1);
+        *reinterpret_cast<u32x2_t*>(Pth + off) = hi;
+        *reinterpret_cast<u32x2_t*>(Ptl + off) = lo;
+        if (kb == qb && !(qb & 1)) {  // even diagonal: keys 16..31 of the step are future
+          const int offz = (base + 16 * (2 + (lg >> 1)) + li) * 8 + 4 * (lg & 1);
+          *reinterpret_cast<u32x2_t*>(Pth + offz) = u32x2_t{0, 0};
+          *reinterpret_cast<u32x2_t*>(Ptl + offz) = u32x2_t{0, 0};
         }
       }
-      __syncthreads();  // all P^T fragments written
+
+      u32x4_t vfr[G::WT][G::KSC];
+      load_vfr(Vs, vfr);
+
+      // S_{c-1} as hi/lo bf16 A-operands of S^T (value row w, 8 keys)
+      u32x4_t sfh[G::WT][G::KSD], sfl[G::WT][G::KSD];
+#pragma unroll
+      for (int wt = 0; wt < G::WT; ++wt)
+#pragma unroll
+        for (int ks = 0; ks < G::KSD; ++ks) {
+          u32x2_t h0, l0, h1, l1;
+          split4(S[wt][2 * ks], h0, l0);
+          split4(S[wt][2 * ks + 1], h1, l1);
+          sfh[wt][ks] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
+          sfl[wt][ks] = u32x4_t{l0[0], l0[1], l1[0], l1[1]};
+        }
+
+      state_update(Ks, vfr, n);
+
+      lds_barrier();  // P^T fragments written; K and V tiles are dead
+      if (more) {
+        load_direct(kg, Ks, tc + C, n_next);
+        load_direct(vg, Vs, tc + C, n_next);
+      }
 
       // ---- outputs: O^T = diag(a) (S^T Q^T) + V^T P^T, per query block ----
-#pragma unroll
+#pragma unroll 1
       for (int qb = 0; qb < G::NQB; ++qb) {
         // Q^T as B operand in the key order of the S fragments:
         // features {32ks + 4lg + r} and {32ks + 16 + 4lg + r}
         u32x4_t qf[G::KSD];
 #pragma unroll
         for (int ks = 0; ks < G::KSD; ++ks) {
-          const uint16_t* row = Qs + (16 * qb + li) * G::QS + 32 * ks + 4 * lg;
-          const u32x2_t a0 = lds_read8(row), a1 = lds_read8(row + 16);
+          const int row = 16 * qb + li;
+          const u32x2_t a0 = lds_read8(Qs + swz<D>(row, 32 * ks + 4 * lg));
+          const u32x2_t a1 = lds_read8(Qs + swz<D>(row, 32 * ks + 16 + 4 * lg));
           qf[ks] = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
         }
         u32x4_t pfh[G::KSC], pfl[G::KSC];
 #pragma unroll
-        for (int ks = 0; ks <= qb / 2; ++ks) {
-          const int off = ((frag_base(qb) + ks) * 64 + lane) * 8;
-          pfh[ks] = lds_read16(Pth + off);
-          pfl[ks] = lds_read16(Ptl + off);
+        for (int ks = 0; ks < G::KSC; ++ks) {
+          if (ks <= qb / 2) {
+            const int off = ((frag_base(qb) + ks) * 64 + lane) * 8;
+            pfh[ks] = lds_read16(Pth + off);
+            pfl[ks] = lds_read16(Ptl + off);
+          }
         }
         const int i = 16 * qb + li;
+        const float aq = fast_exp2(-sl2 * (float)(i + 1));
+        f32x4_t acc[G::WT], acl[G::WT];
 #pragma unroll
         for (int wt = 0; wt < G::WT; ++wt) {
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+          acc[wt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          acl[wt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-          for (int ks = 0; ks < G::KSD; ++ks) {
-            acc = mfma16(sfh[wt][ks], qf[ks], acc);
-            acc = mfma16(sfl[wt][ks], qf[ks], acc);
+        for (int ks = 0; ks < G::KSD; ++ks)
+#pragma unroll
+          for (int wt = 0; wt < G::WT; ++wt) {
+            acc[wt] = mfma16(sfh[wt][ks], qf[ks], acc[wt]);
+            acl[wt] = mfma16(sfl[wt][ks], qf[ks], acl[wt]);
           }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r] *= aq[qb];
+        for (int wt = 0; wt < G::WT; ++wt)
 #pragma unroll
-          for (int ks = 0; ks <= qb / 2; ++ks) {
-            acc = mfma16(vfr[wt][ks], pfh[ks], acc);
-            acc = mfma16(vfr[wt][ks], pfl[ks], acc);
+          for (int r = 0; r < 4; ++r) acc[wt][r] = (acc[wt][r] + acl[wt][r]) * aq;
+#pragma unroll
+        for (int ks = 0; ks < G::KSC; ++ks) {
+          if (ks <= qb / 2) {
+#pragma unroll
+            for (int wt = 0; wt < G::WT; ++wt) {
+              acc[wt] = mfma16(vfr[wt][ks], pfh[ks], acc[wt]);
+              acc[wt] = mfma16(vfr[wt][ks], pfl[ks], acc[wt]);
+            }
           }
-          if (i < n) {
+        }
+        if (i < n) {
+#pragma unroll
+          for (int wt = 0; wt < G::WT; ++wt) {
             uint16_t* dst = og + (size_t)tok(tc + i) * D + 16 * (wave * G::WT + wt) + 4 * lg;
-            *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{pack2(acc[0], acc[1]), pack2(acc[2], acc[3])};
+            *reinterpret_cast<u32x2_t*>(dst) =
+                u32x2_t{pack2(acc[wt][0], acc[wt][1]), pack2(acc[wt][2], acc[wt][3])};
           }
         }
       }
+      lds_barrier();  // Q and P^T tiles are free for the next chunk
     }
-    __syncthreads();  // LDS free for the next chunk
   }
 
   if (s_final) {
