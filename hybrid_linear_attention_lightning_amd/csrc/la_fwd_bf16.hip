@@ -111,8 +111,18 @@ __global__ __launch_bounds__(D / 16 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
   const float* s_init = nullptr;
   float* s_final = nullptr;
   if constexpr (STATE_ONLY) {
-    const int piece = blockIdx.x % pp.npiece;
-    bh = blockIdx.x / pp.npiece;
+    // Pieces are numbered by distance from the end of their segment first:
+    // the pieces every head needs (those just before a segment start) take
+    // the lowest workgroup ids, so they are dispatched first and spread over
+    // all XCDs (consecutive ids go to different XCDs), and the workgroups
+    // that exit at once come last.
+    const int ppseg = pp.seg_len / pp.piece_len;
+    const int groups = pp.B * pp.H * (pp.nseg - 1);
+    const int rank = blockIdx.x / groups;  // 0 = last piece of its segment
+    const int g = blockIdx.x - rank * groups;
+    const int sidx = g % (pp.nseg - 1);
+    const int piece = sidx * ppseg + (ppseg - 1 - rank);
+    bh = g / (pp.nseg - 1);
     H = pp.H;
     N = pp.N;
     reverse = pp.reverse;

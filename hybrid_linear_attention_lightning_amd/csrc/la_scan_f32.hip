@@ -38,20 +38,32 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanPass p) {
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
   if (p.state_in) s = reinterpret_cast<const f32x4_t*>(p.state_in + bh * dd)[e4];
   const float gL = exp2f(-sl2 * (float)p.seg_len);
+  // Every segment but the last is full, so the pieces that segment r-1
+  // contributes to the start of segment r are the same ranks for every r:
+  // rank k (k pieces between it and the segment end) is at distance k * Lp,
+  // and it was computed iff lambda^(k Lp) >= 2^-kSkipLog2 (the test the piece
+  // kernel makes, in the same arithmetic).
   const int ppseg = p.seg_len / p.piece_len;
+  int nneed = 0;
+  while (nneed < ppseg && !(sl2 * (float)(nneed * p.piece_len) >= kSkipLog2)) ++nneed;
+  const f32x4_t* pc4 = reinterpret_cast<const f32x4_t*>(p.pieces + (size_t)bh * p.npiece * dd);
   for (int r = 1; r < p.nseg; ++r) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) s[c] *= gL;
-    const int start = r * p.seg_len;
-    for (int pc = (r - 1) * ppseg; pc < r * ppseg; ++pc) {
-      const int end = min(p.N, (pc + 1) * p.piece_len);
-      const float gap = (float)(start - end);
-      if (sl2 * gap >= kSkipLog2) continue;  // piece was not computed
-      const float f = exp2f(-sl2 * gap);
-      const f32x4_t v =
-          reinterpret_cast<const f32x4_t*>(p.pieces + ((size_t)bh * p.npiece + pc) * dd)[e4];
+    const int last = r * ppseg - 1;  // piece of rank 0
+    for (int k0 = 0; k0 < nneed; k0 += 8) {
+      // eight independent loads in flight, then the weighted sum
+      f32x4_t v[8];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) s[c] = fmaf(f, v[c], s[c]);
+      for (int j = 0; j < 8; ++j)
+        v[j] = k0 + j < nneed ? pc4[(size_t)(last - k0 - j) * (dd / 4) + e4]
+                              : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float f = exp2f(-sl2 * (float)((k0 + j) * p.piece_len));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) s[c] = fmaf(f, v[j][c], s[c]);
+      }
     }
     reinterpret_cast<f32x4_t*>(p.seg_states + ((size_t)bh * p.nseg + r) * dd)[e4] = s;
   }
