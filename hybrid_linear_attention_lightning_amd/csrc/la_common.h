@@ -76,6 +76,20 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// The value of x, hidden from the optimizer (an empty asm that "may change"
+// it): keeps address arithmetic from being hoisted or folded across the
+// point where it is called.  opaque_s keeps a wave-uniform value in an SGPR.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ uint32_t opaque_s(uint32_t x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+// x, known to be the same in every lane, as a scalar value
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // 2^x without the denormal-range fix-up of exp2f (v_exp_f32; results below
 // 2^-126 flush to zero, which the decay factors tolerate).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

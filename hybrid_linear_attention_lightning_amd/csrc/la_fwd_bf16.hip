@@ -12,14 +12,22 @@
 // for Lightning Attention": the state recursion unfolded into matrix form).
 //
 // Design (MI355X):
-//  * one workgroup of d/16 waves owns a whole head (all d value columns) over one
-//    segment of the sequence, so Q K^T is computed once per chunk and every
-//    operand is read from HBM once; parallelism beyond B*H comes from segments,
-//    whose start states the piece and scan kernels assemble (the "local
-//    recursion + global correction" algebra of the same section);
-//  * each wave owns one tile of 16 value columns of the fp32 state, kept in
-//    registers for the whole segment; two waves per SIMD hide each other's
-//    latencies;
+//  * one workgroup of d/32 waves owns a whole head over one segment of the
+//    sequence, so Q K^T is computed once per chunk and every operand is read
+//    from HBM once; parallelism beyond B*H comes from segments, whose start
+//    states the piece and scan kernels assemble (the "local recursion +
+//    global correction" algebra of the same section);
+//  * wave w owns value columns 32w .. 32w+31: its slice of the fp32 state
+//    lives in its registers for the whole segment and it computes every
+//    output and state element of those columns.  Operands shared by all
+//    columns (Q, K and the masked scores) are read from LDS once per wave, so
+//    wider column slices mean less LDS traffic; at one wave per SIMD each
+//    phase is unrolled so that a wave keeps loads, matrix-core and vector
+//    work in flight together;
+//  * the masked scores P^T = (K Q^T) * M^T are computed once per chunk -- wave
+//    w takes the score tiles of query blocks w and NQB-1-w, reusing each K
+//    fragment for both -- and exchanged through LDS in the register order of
+//    the P V product's B operand;
 //  * the three operands that are not inputs -- the masked scores P, the state
 //    S and b*V -- are handed to the matrix cores as bf16 hi + lo pairs, so the
 //    products carry ~16 significant bits (plain bf16 operands would lose as
@@ -30,16 +38,16 @@
 //    constant plus a compile-time offset; K^T and V^T fragments (contractions
 //    over tokens) come straight from the row-major tiles through the
 //    transposing LDS read of gfx950; K and V move global -> LDS without
-//    registers; the masked scores of a chunk are exchanged between waves
-//    through LDS in the exact register order of the MFMA B operand.
+//    registers, Q goes global -> registers one chunk ahead.
 // The same kernel in STATE_ONLY mode computes piece states (K^T diag(b) V
 // accumulated over a piece) for the segment pre-pass.
+#include <type_traits>
+
 #include "la_common.h"
 #include "la_internal.h"
 
 namespace la {
 namespace {
-
 
 __host__ __device__ constexpr int frag_base(int qb) {
   // number of 32-key P^T fragments that query blocks 0..qb-1 use (qb/2+1 each)
@@ -48,28 +56,26 @@ __host__ __device__ constexpr int frag_base(int qb) {
 
 template <int C, int D, bool STATE_ONLY>
 struct Cfg {
-  static constexpr int NW = D / 16;    // waves: one 16-column value tile each
+  static constexpr int NW = D / 32;    // waves: 32 value columns each
   static constexpr int THREADS = 64 * NW;
+  static constexpr int CT = 2;         // 16-column value tiles per wave
   static constexpr int NQB = C / 16;   // 16-token query / key blocks per chunk
   static constexpr int KSC = C / 32;   // 32-token contraction steps
   static constexpr int KSD = D / 32;   // 32-feature contraction steps
-  static constexpr int NT = D / 16;    // 16-feature tiles (key and value side)
-  static constexpr int WT = NT / NW;   // value tiles owned by each wave (1)
+  static constexpr int NT = D / 16;    // 16-feature tiles of the state
+  static constexpr int NPAIR = (NQB + 1) / 2;  // query-block pairs {p, NQB-1-p}
   static constexpr int NFRAG = frag_base(NQB);
   static constexpr int CPR = D / 8;    // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR; // rows per wave-wide 16-byte-per-lane move
-  static constexpr int QCH = C * CPR / THREADS;   // Q chunks per thread (>= 1)
-  static constexpr int NTILE = NQB * (NQB + 1) / 2;       // causal 16x16 score tiles
-  static constexpr int MAXT = (NTILE + NW - 1) / NW;      // score tiles per wave
+  static constexpr int QCH = C * CPR / THREADS;   // Q chunks per thread
   static constexpr int TILE = C * D;              // elements per tile
   static constexpr int PT_HALF = NFRAG * 64 * 8;  // one of P_hi / P_lo
-  // STATE_ONLY: K, V double-buffered; otherwise K, V, Q and the P^T exchange
-  static constexpr int LDS_ELEMS = STATE_ONLY ? 4 * TILE : 3 * TILE + 2 * PT_HALF;
   static_assert(C == 32 || C == 64 || C == 128, "chunk");
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(QCH >= 1, "tile smaller than one chunk per thread");
-  static_assert(WT == 1, "one value tile per wave");
   static_assert((RPI * NW) % 16 == 0 && (THREADS / CPR) % 16 == 0, "row mod 16 per lane");
+  static_assert(C % (RPI * NW) == 0, "whole direct moves per wave");
+  static_assert((STATE_ONLY ? 4 * TILE : 3 * TILE + 2 * PT_HALF) * 2 <= 160 * 1024, "LDS");
 };
 
 // Swizzle of the 16-byte chunk index of row r of a [C][D] bf16 tile.  It
@@ -83,24 +89,15 @@ __host__ __device__ constexpr int swz_of(int r) {
   return ((r >> 1) & 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 1) | (((r >> 3) & 1) << 2);
 }
 
-// (key block, query block) of causal score tile number t, tiles numbered
-// along query blocks: t = qb (qb + 1) / 2 + kb, kb <= qb.  Wave w computes
-// tiles w, w + NW, w + 2 NW, ...
-__device__ __forceinline__ void tile_of(int t, int& kb, int& qb) {
-  int q = 0;
-  while ((q + 1) * (q + 2) / 2 <= t) ++q;
-  qb = q;
-  kb = t - q * (q + 1) / 2;
-}
-
 template <int C, int D, bool STATE_ONLY>
-__global__ __launch_bounds__(D / 16 * 64) void fwd_bf16_kernel(FwdPass p, PiecePass pp) {
+__global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PiecePass pp) {
   using G = Cfg<C, D, STATE_ONLY>;
   constexpr int kThreads = G::THREADS;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[G::LDS_ELEMS];
+  constexpr int CT = G::CT;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const int wave = uniform(tid >> 6);
+  const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
 
   // ---- work item -------------------------------------------------------
   int bh, tau0, tau_end, N, H;
@@ -160,9 +157,20 @@ __global__ __launch_bounds__(D / 16 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
     if (seg == p.nseg - 1 && p.state_out) s_final = p.state_out + (size_t)bh * D * D;
   }
   const float sl2 = slope[bh % H] * kLog2e;  // lambda^e = exp2(-sl2 * e)
+  const int col0 = 32 * wave;                // this wave's first value column
+
+  // ---- fp32 state: S[t][ct][r] = S[feature 16t + 4lg + r][value col0 + 16ct + li]
+  f32x4_t S[G::NT][CT];
+#pragma unroll
+  for (int t = 0; t < G::NT; ++t)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        S[t][ct][r] = s_init ? s_init[(size_t)(16 * t + 4 * lg + r) * D + col0 + 16 * ct + li] : 0.f;
 
   // ---- per-lane decay tables --------------------------------------------
-  // P^T tile element: key row j = 16kb + 4lg + r, query column i = 16qb + li.
+  // P^T tile element: key row 16kb + 4lg + r, query column 16qb + li.
   // Diagonal tiles use md (zero above the diagonal); off-diagonal tiles use
   // lambda^(16 (qb-kb-1)) * mo[r], both factors <= 1 so nothing overflows.
   float md[4], mo[4];
@@ -177,188 +185,207 @@ __global__ __launch_bounds__(D / 16 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
   float bl[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) bl[e] = fast_exp2(-sl2 * (float)(31 - 8 * lg - e));
+  // a of query 16qb + li is a_lane * lambda^(16 qb)
+  const float a_lane = fast_exp2(-sl2 * (float)(li + 1));
 
   // ---- per-lane LDS offsets (elements); loop indices add constants ------
-  // row fragments: rows 16kb + li, features 32ks + 8lg .. +8  (+ 16kb*D)
+  // row fragments (16 B): rows 16x + li, features 32ks + 8lg .. +7
   const int sA = swz_of<D>(li);
   int offA[G::KSD];
 #pragma unroll
   for (int ks = 0; ks < G::KSD; ++ks) offA[ks] = li * D + 8 * ((4 * ks + lg) ^ sA);
-  // permuted Q fragments: row 16qb + li, features 32ks + 16hh + 4lg .. +4  (+ 16qb*D)
+  // permuted Q fragments (2 x 8 B): row 16qb + li, features 32ks + 16hh + 4lg .. +3
   int offC[G::KSD][2];
 #pragma unroll
   for (int ks = 0; ks < G::KSD; ++ks)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
       offC[ks][hh] = li * D + 8 * ((4 * ks + (lg >> 1) + 2 * hh) ^ sA) + 4 * (lg & 1);
-  // transposing reads: row 32ks + 8lg + (li>>2) + 4hh, column 16t + 4(li&3)  (+ 32ks*D)
+  // transposing reads: row 8lg + (li>>2) + 4hh (+32ks), columns 16t + 4(li&3) .. +3;
+  // the lane group's lane i then receives column 16t + i of those 4 rows
   auto off_tr = [&](int hh, int t) {
     const int r = 8 * lg + (li >> 2) + 4 * hh;
     return r * D + 8 * ((2 * t + ((li & 3) >> 1)) ^ swz_of<D>(r & 15)) + 4 * (li & 1);
   };
-  // column fragment (8 tokens 32ks + 8lg .., one feature column) from two
-  // transposing reads at tile + o0 and tile + o1
-  auto col_frag = [&](const uint16_t* tile, int o0, int o1) -> u32x4_t {
-    const u32x2_t a = lds_read_tr8(tile + o0);
-    const u32x2_t c = lds_read_tr8(tile + o1);
+  int offT[G::NT][2], offV[CT][2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+    for (int t = 0; t < G::NT; ++t) offT[t][hh] = off_tr(hh, t);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) offV[ct][hh] = off_tr(hh, 2 * wave + ct);
+  }
+  // The per-lane offsets are re-issued at the top of every chunk through an
+  // empty asm, so the compiler cannot hoist the dozens of addresses derived
+  // from them out of the chunk loop, where they would stay live and spill.
+  int lA[G::KSD], lC[G::KSD][2], lT[G::NT][2], lV[CT][2];
+  auto refresh_offsets = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < G::KSD; ++ks) {
+      lA[ks] = opaque(offA[ks]);
+      lC[ks][0] = opaque(offC[ks][0]);
+      lC[ks][1] = opaque(offC[ks][1]);
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int t = 0; t < G::NT; ++t) lT[t][hh] = opaque(offT[t][hh]);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) lV[ct][hh] = opaque(offV[ct][hh]);
+    }
+  };
+
+  // column fragment: 8 tokens 32ks + 8lg .. +7 of one column, from two
+  // transposing reads
+  auto col_frag = [&](const uint16_t* tile, int ks, const int (&o)[2]) -> u32x4_t {
+    const u32x2_t a = lds_read_tr8(tile + 32 * ks * D + o[0]);
+    const u32x2_t c = lds_read_tr8(tile + 32 * ks * D + o[1]);
     return u32x4_t{a[0], a[1], c[0], c[1]};
   };
 
-  // ---- fp32 state: this wave's WT value tiles x NT key tiles ------------
-  // S[wt][t][r] = S[key 16t + 4lg + r][value 16(wave*WT + wt) + li]
-  f32x4_t S[G::WT][G::NT];
-  if (s_init) {
-#pragma unroll
-    for (int wt = 0; wt < G::WT; ++wt)
-#pragma unroll
-      for (int t = 0; t < G::NT; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          S[wt][t][r] = s_init[(size_t)(16 * t + 4 * lg + r) * D + 16 * (wave * G::WT + wt) + li];
-  } else {
-#pragma unroll
-    for (int wt = 0; wt < G::WT; ++wt)
-#pragma unroll
-      for (int t = 0; t < G::NT; ++t) S[wt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-
   // ---- staging ------------------------------------------------------------
-  // K and V go global -> LDS directly (no registers), each into a tile that
-  // is dead by the time the load is issued; Q goes global -> registers one
-  // chunk ahead -> swizzled LDS at the top of the next chunk.  Rows past the
-  // end of the sequence read the last valid row: such K and V rows only ever
-  // meet zero weights (causal mask, b = 0), and Q rows past the end produce
-  // outputs that are not stored.
-  const long rstep = reverse ? -(long)D : (long)D;  // elements between positions
-  auto pos_ptr = [&](const uint16_t* base, int tau) {
-    return base + (long)(reverse ? (N - 1 - tau) : tau) * D;
-  };
-  // Direct moves: wave instruction j covers rows RPI*j .. RPI*j + RPI-1 (the
-  // wave's instructions are j = wave, wave+NW, ..., and RPI*NW is a multiple
-  // of 16, so row mod 16 is fixed per lane); lane l lands in physical chunk
-  // l % CPR of row RPI*j + l / CPR and fetches the logical chunk the swizzle
-  // maps there.
-  const int dm_row = lane / G::CPR;
-  const int dm_col = 8 * ((lane % G::CPR) ^ swz_of<D>((G::RPI * wave + dm_row) & 15));
+  // Rows past the end of the sequence read the last valid row: such K and V
+  // rows only ever meet zero weights (causal mask, b = 0), and Q rows past
+  // the end produce outputs that are not stored.
+  //
+  // Direct moves: the wave's instruction m covers rows RPI (wave + NW m) ..
+  // +RPI-1 of the tile; lane l lands in physical chunk l % CPR of the row
+  // RPI (wave + NW m) + l / CPR and fetches the logical chunk the swizzle maps
+  // there (RPI NW is a multiple of 16, so row mod 16 is fixed per lane).
+  // Global offsets count from the chunk's lowest-address token, so they are
+  // non-negative in both directions.  The LDS destination goes to the
+  // instruction as a plain address (through an empty asm), so the compiler
+  // does not tie these writes to the tile variables and does not hold later
+  // LDS reads of other tiles until they land; the kernel waits for them
+  // itself (vmcnt(0) and a barrier before the tile is read).
+  constexpr int DM_STEP = G::RPI * G::NW;  // rows between a lane's moves
+  constexpr int DM_N = C / DM_STEP;        // moves per wave and tile
+  const int dm_row0 = G::RPI * wave + lane / G::CPR;
+  const int dm_col = 8 * ((lane % G::CPR) ^ swz_of<D>(dm_row0 & 15));
+  const int dm_off = (reverse ? (C - 1 - dm_row0) : dm_row0) * D + dm_col;
+  const int dm_step = reverse ? -DM_STEP * D : DM_STEP * D;
   auto load_direct = [&](const uint16_t* src, uint16_t* tile, int tc, int n) {
-    const uint16_t* base = pos_ptr(src, tc) + dm_col;
+    const uint16_t* base = src + (long)(reverse ? (N - tc - n) : tc) * D;
+    const uint32_t lds0 = opaque_s((uint32_t)(uintptr_t)(tile + G::RPI * wave * D));
+    constexpr uint32_t kMoveBytes = 2u * G::RPI * G::NW * D;  // LDS bytes between moves
+    if (n == C) {
 #pragma unroll
-    for (int j = wave; j < C / G::RPI; j += G::NW) {
-      const int row = G::RPI * j + dm_row;
-      __builtin_amdgcn_global_load_lds(
-          base + (long)min(row, n - 1) * rstep,
-          (__attribute__((address_space(3))) void*)(tile + G::RPI * j * D), 16, 0, 0);
-    }
-  };
-  // Q: thread chunk m is row tid/CPR + (256/CPR) m, chunk tid % CPR
-  const int qrow = tid / G::CPR;
-  const int qoff = qrow * D + 8 * ((tid % G::CPR) ^ swz_of<D>(qrow & 15));
-  u32x4_t qstg[G::QCH];
-  auto load_q = [&](int tc, int n) {
-    const uint16_t* base = pos_ptr(qg, tc) + 8 * (tid % G::CPR);
+      for (int m = 0; m < DM_N; ++m)
+        __builtin_amdgcn_global_load_lds(
+            base + (dm_off + m * dm_step),
+            (__attribute__((address_space(3))) void*)(uintptr_t)(lds0 + kMoveBytes * m), 16, 0, 0);
+    } else {
 #pragma unroll
-    for (int m = 0; m < G::QCH; ++m) {
-      const int row = qrow + (kThreads / G::CPR) * m;
-      qstg[m] = *reinterpret_cast<const u32x4_t*>(base + (long)min(row, n - 1) * rstep);
+      for (int m = 0; m < DM_N; ++m) {
+        const int rr = min(dm_row0 + DM_STEP * m, n - 1);
+        __builtin_amdgcn_global_load_lds(
+            base + ((reverse ? (n - 1 - rr) : rr) * D + dm_col),
+            (__attribute__((address_space(3))) void*)(uintptr_t)(lds0 + kMoveBytes * m), 16, 0, 0);
+      }
     }
   };
 
-  // S <- lambda^n S + K^T diag(b) V for the chunk in (Kt, V fragments vfr)
-  int offTK[G::NT][2];
+  // V^T fragments of this wave's value tiles, all token steps of the chunk
+  auto load_vfr = [&](const uint16_t* Vt, u32x4_t (&vf)[G::KSC][CT]) {
 #pragma unroll
-  for (int t = 0; t < G::NT; ++t) {
-    offTK[t][0] = off_tr(0, t);
-    offTK[t][1] = off_tr(1, t);
-  }
-  auto state_update = [&](const uint16_t* Kt, const u32x4_t (&vfr)[G::WT][G::KSC], int n) {
+    for (int ks = 0; ks < G::KSC; ++ks)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) vf[ks][ct] = col_frag(Vt, ks, lV[ct]);
+  };
+
+  // S <- lambda^n S + K^T diag(b) V for the chunk (K tile Kt, V fragments vf)
+  auto state_update = [&](const uint16_t* Kt, const u32x4_t (&vf)[G::KSC][CT], int n) {
     const float gdec = fast_exp2(-sl2 * (float)n);
 #pragma unroll
-    for (int wt = 0; wt < G::WT; ++wt)
+    for (int t = 0; t < G::NT; ++t)
 #pragma unroll
-      for (int t = 0; t < G::NT; ++t)
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[wt][t][r] *= gdec;
+        for (int r = 0; r < 4; ++r) S[t][ct][r] *= gdec;
 #pragma unroll
     for (int ks = 0; ks < G::KSC; ++ks) {
-      float bks[8];
+      float bk[8];
       if (n == C) {
         const float f = fast_exp2(-sl2 * (float)(32 * (G::KSC - 1 - ks)));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bks[e] = f * bl[e];
+        for (int e = 0; e < 8; ++e) bk[e] = f * bl[e];
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int x = 32 * ks + 8 * lg + e;
-          bks[e] = x < n ? fast_exp2(-sl2 * (float)(n - 1 - x)) : 0.f;
+          const int x = 32 * ks + 8 * opaque(lg) + e;
+          bk[e] = x < n ? fast_exp2(-sl2 * (float)(n - 1 - x)) : 0.f;
         }
       }
-      u32x4_t vbh[G::WT], vbl[G::WT];
+      u32x4_t bvh[CT], bvl[CT];
 #pragma unroll
-      for (int wt = 0; wt < G::WT; ++wt) {
+      for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const uint32_t w0 = vfr[wt][ks][2 * c], w1 = vfr[wt][ks][2 * c + 1];
-          const f32x4_t x = {bf_lo(w0) * bks[4 * c], bf_hi(w0) * bks[4 * c + 1],
-                             bf_lo(w1) * bks[4 * c + 2], bf_hi(w1) * bks[4 * c + 3]};
-          u32x2_t hh, ll;
-          split4(x, hh, ll);
-          vbh[wt][2 * c] = hh[0];
-          vbh[wt][2 * c + 1] = hh[1];
-          vbl[wt][2 * c] = ll[0];
-          vbl[wt][2 * c + 1] = ll[1];
+          const uint32_t w0 = vf[ks][ct][2 * c], w1 = vf[ks][ct][2 * c + 1];
+          const f32x4_t x = {bf_lo(w0) * bk[4 * c], bf_hi(w0) * bk[4 * c + 1],
+                             bf_lo(w1) * bk[4 * c + 2], bf_hi(w1) * bk[4 * c + 3]};
+          u32x2_t h2, l2;
+          split4(x, h2, l2);
+          bvh[ct][2 * c] = h2[0];
+          bvh[ct][2 * c + 1] = h2[1];
+          bvl[ct][2 * c] = l2[0];
+          bvl[ct][2 * c + 1] = l2[1];
         }
       }
-      const uint16_t* Kk = Kt + 32 * ks * D;
 #pragma unroll
       for (int t = 0; t < G::NT; ++t) {
-        const u32x4_t kf = col_frag(Kk, offTK[t][0], offTK[t][1]);
+        const u32x4_t kt = col_frag(Kt, ks, lT[t]);
 #pragma unroll
-        for (int wt = 0; wt < G::WT; ++wt) S[wt][t] = mfma16(kf, vbh[wt], S[wt][t]);
+        for (int ct = 0; ct < CT; ++ct) S[t][ct] = mfma16(kt, bvh[ct], S[t][ct]);
 #pragma unroll
-        for (int wt = 0; wt < G::WT; ++wt) S[wt][t] = mfma16(kf, vbl[wt], S[wt][t]);
+        for (int ct = 0; ct < CT; ++ct) S[t][ct] = mfma16(kt, bvl[ct], S[t][ct]);
       }
-    }
-  };
-
-  auto load_vfr = [&](const uint16_t* Vt, u32x4_t (&vfr)[G::WT][G::KSC]) {
-#pragma unroll
-    for (int wt = 0; wt < G::WT; ++wt) {
-      const int o0 = off_tr(0, wave * G::WT + wt), o1 = off_tr(1, wave * G::WT + wt);
-#pragma unroll
-      for (int ks = 0; ks < G::KSC; ++ks) vfr[wt][ks] = col_frag(Vt + 32 * ks * D, o0, o1);
     }
   };
 
   if constexpr (STATE_ONLY) {
-    // K and V double-buffered: chunk c+1 streams in while chunk c is used
-    int buf = 0;
-    if (tau0 < tau_end) {
-      load_direct(kg, smem, tau0, min(C, tau_end - tau0));
-      load_direct(vg, smem + G::TILE, tau0, min(C, tau_end - tau0));
-    }
-    for (int tc = tau0; tc < tau_end; tc += C) {
+    // K and V double-buffered: chunk c+1 streams in while chunk c is used.
+    // Each buffer is its own variable and the loop is unrolled by two, so
+    // every LDS read names its buffer statically.
+    __shared__ __attribute__((aligned(16))) uint16_t K0[G::TILE], V0[G::TILE], K1[G::TILE],
+        V1[G::TILE];
+    auto chunk = [&](auto par, int tc) {
+      constexpr int PAR = decltype(par)::value;
+      refresh_offsets();
       const int n = min(C, tau_end - tc);
-      uint16_t* Kc = smem + (2 * buf) * G::TILE;
-      uint16_t* Vc = Kc + G::TILE;
       __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk tc have landed
-      lds_barrier();
+      lds_barrier();                  // ... everyone's, and chunk tc - C is done
       if (tc + C < tau_end) {
-        uint16_t* Kn = smem + (2 * (buf ^ 1)) * G::TILE;
-        load_direct(kg, Kn, tc + C, min(C, tau_end - tc - C));
-        load_direct(vg, Kn + G::TILE, tc + C, min(C, tau_end - tc - C));
+        load_direct(kg, PAR ? K0 : K1, tc + C, min(C, tau_end - tc - C));
+        load_direct(vg, PAR ? V0 : V1, tc + C, min(C, tau_end - tc - C));
       }
-      u32x4_t vfr[G::WT][G::KSC];
-      load_vfr(Vc, vfr);
-      state_update(Kc, vfr, n);
-      lds_barrier();  // chunk tc's tiles are free for chunk tc + 2C
-      buf ^= 1;
+      u32x4_t vf[G::KSC][CT];
+      load_vfr(PAR ? V1 : V0, vf);
+      state_update(PAR ? K1 : K0, vf, n);
+    };
+    if (tau0 < tau_end) {
+      load_direct(kg, K0, tau0, min(C, tau_end - tau0));
+      load_direct(vg, V0, tau0, min(C, tau_end - tau0));
+    }
+    for (int tc = tau0; tc < tau_end; tc += 2 * C) {
+      chunk(std::integral_constant<int, 0>{}, tc);
+      if (tc + C < tau_end) chunk(std::integral_constant<int, 1>{}, tc + C);
     }
   } else {
-    uint16_t* Ks = smem;
-    uint16_t* Vs = Ks + G::TILE;
-    uint16_t* Qs = Vs + G::TILE;
-    uint16_t* Pth = Qs + G::TILE;
-    uint16_t* Ptl = Pth + G::PT_HALF;
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[G::TILE], Vs[G::TILE], Qs[G::TILE],
+        Pth[G::PT_HALF], Ptl[G::PT_HALF];
+    // Q: thread chunk m is row tid/CPR + (THREADS/CPR) m, chunk tid % CPR
+    const int qrow = tid / G::CPR;
+    const int qoff = qrow * D + 8 * ((tid % G::CPR) ^ swz_of<D>(qrow & 15));
+    u32x4_t qstg[G::QCH];
+    auto load_q = [&](int tc, int n) {
+      const uint16_t* base = qg + (long)(reverse ? (N - tc - n) : tc) * D + 8 * (tid % G::CPR);
+#pragma unroll
+      for (int m = 0; m < G::QCH; ++m) {
+        const int rr = min(qrow + (kThreads / G::CPR) * m, n - 1);
+        qstg[m] = *reinterpret_cast<const u32x4_t*>(base + (reverse ? (n - 1 - rr) : rr) * D);
+      }
+    };
     if (tau0 < tau_end) {
       const int n0 = min(C, tau_end - tau0);
       load_direct(kg, Ks, tau0, n0);
@@ -369,6 +396,7 @@ __global__ __launch_bounds__(D / 16 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
       const int n = min(C, tau_end - tc);
       const bool more = tc + C < tau_end;
       const int n_next = more ? min(C, tau_end - tc - C) : 0;
+      refresh_offsets();
 #pragma unroll
       for (int m = 0; m < G::QCH; ++m)
         *reinterpret_cast<u32x4_t*>(Qs + qoff + (kThreads / G::CPR) * m * D) = qstg[m];
@@ -376,20 +404,20 @@ __global__ __launch_bounds__(D / 16 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
       lds_barrier();                  // chunk tc is in LDS
       if (more) load_q(tc + C, n_next);
 
+      u32x4_t vf[G::KSC][CT];
+      load_vfr(Vs, vf);
+
       // ---- masked scores P^T = (K Q^T) * M^T -> LDS as hi/lo B fragments ----
       // Tile (kb, qb), lane (lg, li) holds keys 16kb + 4lg + r of query
       // 16qb + li; in the 32-key step kb/2 these are element 4(lg&1) + r of
-      // consumer lane (2(kb&1) + (lg>>1), li).
-#pragma unroll 1
-      for (int t = wave; t < G::NTILE; t += G::NW) {
-        int kb, qb;
-        tile_of(t, kb, qb);
-        const uint16_t* Kb = Ks + 16 * kb * D;
-        const uint16_t* Qb = Qs + 16 * qb * D;
+      // consumer lane (2(kb&1) + (lg>>1), li).  Wave w takes the query-block
+      // pairs {p, NQB-1-p}, p = w, w + NW, ...: NQB+1 tiles per pair, and each
+      // K fragment serves both blocks of the pair.
+      auto score_tile = [&](const u32x4_t (&kf)[G::KSD], const u32x4_t (&qf)[G::KSD], int kb,
+                            int qb) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < G::KSD; ++ks)
-          acc = mfma16(lds_read16(Kb + offA[ks]), lds_read16(Qb + offA[ks]), acc);
+        for (int ks = 0; ks < G::KSD; ++ks) acc = mfma16(kf[ks], qf[ks], acc);
         const int delta = qb - kb;
         if (delta == 0) {
 #pragma unroll
@@ -409,25 +437,40 @@ __global__ __launch_bounds__(D / 16 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
           *reinterpret_cast<u32x2_t*>(Pth + off + 256) = u32x2_t{0, 0};
           *reinterpret_cast<u32x2_t*>(Ptl + off + 256) = u32x2_t{0, 0};
         }
+      };
+      for (int pr = wave; pr < G::NPAIR; pr += G::NW) {
+        const int qlo = pr, qhi = G::NQB - 1 - pr;
+        u32x4_t qfl[G::KSD], qfh[G::KSD];
+#pragma unroll
+        for (int ks = 0; ks < G::KSD; ++ks) {
+          qfl[ks] = lds_read16(Qs + 16 * qlo * D + lA[ks]);
+          qfh[ks] = lds_read16(Qs + 16 * qhi * D + lA[ks]);
+        }
+#pragma unroll 2
+        for (int kb = 0; kb <= qhi; ++kb) {
+          u32x4_t kf[G::KSD];
+#pragma unroll
+          for (int ks = 0; ks < G::KSD; ++ks) kf[ks] = lds_read16(Ks + 16 * kb * D + lA[ks]);
+          score_tile(kf, qfh, kb, qhi);
+          if (kb <= qlo && qlo != qhi) score_tile(kf, qfl, kb, qlo);
+        }
       }
 
-      u32x4_t vfr[G::WT][G::KSC];
-      load_vfr(Vs, vfr);
-
-      // S_{c-1} as hi/lo bf16 A-operands of S^T (value row w, 8 keys)
-      u32x4_t sfh[G::WT][G::KSD], sfl[G::WT][G::KSD];
+      // S_{c-1} as hi/lo bf16 A operands of S^T (value row li, features
+      // {32ks + 4lg + r} and {32ks + 16 + 4lg + r})
+      u32x4_t sfh[CT][G::KSD], sfl[CT][G::KSD];
 #pragma unroll
-      for (int wt = 0; wt < G::WT; ++wt)
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int ks = 0; ks < G::KSD; ++ks) {
           u32x2_t h0, l0, h1, l1;
-          split4(S[wt][2 * ks], h0, l0);
-          split4(S[wt][2 * ks + 1], h1, l1);
-          sfh[wt][ks] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
-          sfl[wt][ks] = u32x4_t{l0[0], l0[1], l1[0], l1[1]};
+          split4(S[2 * ks][ct], h0, l0);
+          split4(S[2 * ks + 1][ct], h1, l1);
+          sfh[ct][ks] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
+          sfl[ct][ks] = u32x4_t{l0[0], l0[1], l1[0], l1[1]};
         }
 
-      state_update(Ks, vfr, n);
+      state_update(Ks, vf, n);
 
       lds_barrier();  // P^T fragments written; K and V tiles are dead
       if (more) {
@@ -436,63 +479,52 @@ __global__ __launch_bounds__(D / 16 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
       }
 
       // ---- outputs: O^T = diag(a) (S^T Q^T) + V^T P^T, per query block ----
-      uint16_t* orow = og + (long)(reverse ? (N - 1 - tc) : tc) * D + 16 * (wave * G::WT) + 4 * lg;
-#pragma unroll 1
+      // outputs are addressed from the chunk's lowest-address token with
+      // 32-bit offsets computed here (li passes through opaque)
+      uint16_t* obase = og + (long)(reverse ? (N - tc - n) : tc) * D + col0;
+      const int li_c = opaque(li);
+      const int o_lane = 4 * lg + (reverse ? (n - 1 - li_c) : li_c) * D;
+      const int o_qb = reverse ? -16 * D : 16 * D;
+#pragma unroll
       for (int qb = 0; qb < G::NQB; ++qb) {
-        // Q^T as B operand in the key order of the S fragments:
-        // features {32ks + 4lg + r} and {32ks + 16 + 4lg + r}
-        const uint16_t* Qb = Qs + 16 * qb * D;
+        // Q^T as B operand in the feature order of the S fragments
         u32x4_t qf[G::KSD];
 #pragma unroll
         for (int ks = 0; ks < G::KSD; ++ks) {
-          const u32x2_t a0 = lds_read8(Qb + offC[ks][0]);
-          const u32x2_t a1 = lds_read8(Qb + offC[ks][1]);
+          const u32x2_t a0 = lds_read8(Qs + 16 * qb * D + lC[ks][0]);
+          const u32x2_t a1 = lds_read8(Qs + 16 * qb * D + lC[ks][1]);
           qf[ks] = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
         }
-        const uint16_t* Pq = Pth + (frag_base(qb) * 64 + lane) * 8;
         u32x4_t pfh[G::KSC], pfl[G::KSC];
 #pragma unroll
-        for (int ks = 0; ks < G::KSC; ++ks) {
-          if (ks <= qb / 2) {
-            pfh[ks] = lds_read16(Pq + ks * 512);
-            pfl[ks] = lds_read16(Pq + G::PT_HALF + ks * 512);
-          }
+        for (int ks = 0; ks <= qb / 2; ++ks) {
+          pfh[ks] = lds_read16(Pth + (frag_base(qb) + ks) * 512 + 8 * lane);
+          pfl[ks] = lds_read16(Ptl + (frag_base(qb) + ks) * 512 + 8 * lane);
         }
-        const int i = 16 * qb + li;
-        const float aq = fast_exp2(-sl2 * (float)(i + 1));
-        f32x4_t acc[G::WT], acl[G::WT];
+        const float aq = a_lane * fast_exp2(-sl2 * (float)(16 * qb));
+        f32x4_t acc[CT];
 #pragma unroll
-        for (int wt = 0; wt < G::WT; ++wt) {
-          acc[wt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          acl[wt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int ct = 0; ct < CT; ++ct) {
+          f32x4_t x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < G::KSD; ++ks)
-#pragma unroll
-          for (int wt = 0; wt < G::WT; ++wt) {
-            acc[wt] = mfma16(sfh[wt][ks], qf[ks], acc[wt]);
-            acl[wt] = mfma16(sfl[wt][ks], qf[ks], acl[wt]);
+          for (int ks = 0; ks < G::KSD; ++ks) {
+            x = mfma16(sfh[ct][ks], qf[ks], x);
+            y = mfma16(sfl[ct][ks], qf[ks], y);
           }
 #pragma unroll
-        for (int wt = 0; wt < G::WT; ++wt)
+          for (int r = 0; r < 4; ++r) acc[ct][r] = (x[r] + y[r]) * aq;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[wt][r] = (acc[wt][r] + acl[wt][r]) * aq;
-#pragma unroll
-        for (int ks = 0; ks < G::KSC; ++ks) {
-          if (ks <= qb / 2) {
-#pragma unroll
-            for (int wt = 0; wt < G::WT; ++wt) {
-              acc[wt] = mfma16(vfr[wt][ks], pfh[ks], acc[wt]);
-              acc[wt] = mfma16(vfr[wt][ks], pfl[ks], acc[wt]);
-            }
+          for (int ks = 0; ks <= qb / 2; ++ks) {
+            acc[ct] = mfma16(vf[ks][ct], pfh[ks], acc[ct]);
+            acc[ct] = mfma16(vf[ks][ct], pfl[ks], acc[ct]);
           }
         }
-        if (i < n) {
-          uint16_t* dst = orow + (long)i * rstep;
+        if (16 * qb + li_c < n) {
+          uint16_t* dst = obase + (o_lane + qb * o_qb);
 #pragma unroll
-          for (int wt = 0; wt < G::WT; ++wt)
-            *reinterpret_cast<u32x2_t*>(dst + 16 * wt) =
-                u32x2_t{pack2(acc[wt][0], acc[wt][1]), pack2(acc[wt][2], acc[wt][3])};
+          for (int ct = 0; ct < CT; ++ct)
+            *reinterpret_cast<u32x2_t*>(dst + 16 * ct) =
+                u32x2_t{pack2(acc[ct][0], acc[ct][1]), pack2(acc[ct][2], acc[ct][3])};
         }
       }
       lds_barrier();  // Q and P^T tiles are free for the next chunk
@@ -501,12 +533,12 @@ __global__ __launch_bounds__(D / 16 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
 
   if (s_final) {
 #pragma unroll
-    for (int wt = 0; wt < G::WT; ++wt)
+    for (int t = 0; t < G::NT; ++t)
 #pragma unroll
-      for (int t = 0; t < G::NT; ++t)
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          s_final[(size_t)(16 * t + 4 * lg + r) * D + 16 * (wave * G::WT + wt) + li] = S[wt][t][r];
+          s_final[(size_t)(16 * t + 4 * lg + r) * D + col0 + 16 * ct + li] = S[t][ct][r];
   }
 }
 
@@ -514,7 +546,7 @@ template <int C, int D>
 hipError_t launch_fwd_cd(const FwdPass& p, hipStream_t s) {
   PiecePass none{};
   const unsigned grid = (unsigned)(p.B * p.H * p.nseg);
-  hipLaunchKernelGGL((fwd_bf16_kernel<C, D, false>), dim3(grid), dim3(D / 16 * 64), 0, s, p, none);
+  hipLaunchKernelGGL((fwd_bf16_kernel<C, D, false>), dim3(grid), dim3(D / 32 * 64), 0, s, p, none);
   return hipGetLastError();
 }
 
@@ -522,7 +554,7 @@ template <int C, int D>
 hipError_t launch_pieces_cd(const PiecePass& pp, hipStream_t s) {
   FwdPass none{};
   const unsigned grid = (unsigned)(pp.B * pp.H * pp.npiece);
-  hipLaunchKernelGGL((fwd_bf16_kernel<C, D, true>), dim3(grid), dim3(D / 16 * 64), 0, s, none, pp);
+  hipLaunchKernelGGL((fwd_bf16_kernel<C, D, true>), dim3(grid), dim3(D / 32 * 64), 0, s, none, pp);
   return hipGetLastError();
 }
 
