@@ -438,15 +438,15 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
           *reinterpret_cast<u32x2_t*>(Ptl + off + 256) = u32x2_t{0, 0};
         }
       };
-      for (int pr = wave; pr < G::NPAIR; pr += G::NW) {
-        const int qlo = pr, qhi = G::NQB - 1 - pr;
+      auto pair_tiles = [&](auto pr_c) {
+        constexpr int qlo = decltype(pr_c)::value, qhi = G::NQB - 1 - qlo;
         u32x4_t qfl[G::KSD], qfh[G::KSD];
 #pragma unroll
         for (int ks = 0; ks < G::KSD; ++ks) {
           qfl[ks] = lds_read16(Qs + 16 * qlo * D + lA[ks]);
           qfh[ks] = lds_read16(Qs + 16 * qhi * D + lA[ks]);
         }
-#pragma unroll 2
+#pragma unroll
         for (int kb = 0; kb <= qhi; ++kb) {
           u32x4_t kf[G::KSD];
 #pragma unroll
@@ -454,6 +454,12 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
           score_tile(kf, qfh, kb, qhi);
           if (kb <= qlo && qlo != qhi) score_tile(kf, qfl, kb, qlo);
         }
+      };
+      for (int pr = wave; pr < G::NPAIR; pr += G::NW) {
+        if (pr == 0) pair_tiles(std::integral_constant<int, 0>{});
+        if constexpr (G::NPAIR > 1) if (pr == 1) pair_tiles(std::integral_constant<int, 1>{});
+        if constexpr (G::NPAIR > 2) if (pr == 2) pair_tiles(std::integral_constant<int, 2>{});
+        if constexpr (G::NPAIR > 3) if (pr == 3) pair_tiles(std::integral_constant<int, 3>{});
       }
 
       // S_{c-1} as hi/lo bf16 A operands of S^T (value row li, features
