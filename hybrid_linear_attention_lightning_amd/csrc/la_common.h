@@ -96,10 +96,22 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // Split four fp32 values into bf16 hi + lo parts (x ~= hi + lo to about 2^-16
 // relative): the matrix cores then see 16 significant bits instead of 8.
+// hi is x rounded to bf16; the residual x - hi is exact in fp32 and comes
+// from one bf16 dot product per value (hi_pair . (-1, 0) + x), with both
+// products exact, instead of unpacking hi and subtracting.
 __device__ __forceinline__ void split4(f32x4_t x, u32x2_t& hi, u32x2_t& lo) {
   const uint32_t h0 = pack2(x[0], x[1]), h1 = pack2(x[2], x[3]);
   hi = u32x2_t{h0, h1};
-  lo = u32x2_t{pack2(x[0] - bf_lo(h0), x[1] - bf_hi(h0)), pack2(x[2] - bf_lo(h1), x[3] - bf_hi(h1))};
+  // (-1, 0) and (0, -1) as bf16 pairs, passed as opaque bit patterns: as
+  // inline constants the packed pair would be encoded as the fp32 constant
+  // -1.0, whose bf16 halves are (0, -1)
+  const bf16x2_t neg_lo = __builtin_bit_cast(bf16x2_t, opaque_s(0x0000BF80u));
+  const bf16x2_t neg_hi = __builtin_bit_cast(bf16x2_t, opaque_s(0xBF800000u));
+  const bf16x2_t p0 = __builtin_bit_cast(bf16x2_t, h0), p1 = __builtin_bit_cast(bf16x2_t, h1);
+  lo = u32x2_t{pack2(__builtin_amdgcn_fdot2_f32_bf16(p0, neg_lo, x[0], false),
+                     __builtin_amdgcn_fdot2_f32_bf16(p0, neg_hi, x[1], false)),
+               pack2(__builtin_amdgcn_fdot2_f32_bf16(p1, neg_lo, x[2], false),
+                     __builtin_amdgcn_fdot2_f32_bf16(p1, neg_hi, x[3], false))};
 }
 
 }  // namespace la

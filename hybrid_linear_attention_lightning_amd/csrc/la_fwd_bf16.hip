@@ -511,14 +511,14 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
         f32x4_t acc[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          f32x4_t x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+          f32x4_t x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < G::KSD; ++ks) {
             x = mfma16(sfh[ct][ks], qf[ks], x);
-            y = mfma16(sfl[ct][ks], qf[ks], y);
+            x = mfma16(sfl[ct][ks], qf[ks], x);
           }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[ct][r] = (x[r] + y[r]) * aq;
+          for (int r = 0; r < 4; ++r) acc[ct][r] = x[r] * aq;
 #pragma unroll
           for (int ks = 0; ks <= qb / 2; ++ks) {
             acc[ct] = mfma16(vf[ks][ct], pfh[ks], acc[ct]);
