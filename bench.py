@@ -33,6 +33,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic():
+    """HBM bytes per launch of the main prefill kernel from the committed
+    FETCH_SIZE / WRITE_SIZE summary, or None when the kernel source has
+    changed since those counters were taken (its sha256 no longer matches)."""
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, "profiles", "prefill_128k_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_t = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
+    m_h = re.search(r"^kernel_source_sha256: ([0-9a-f]{64})$", text, re.M)
+    if not (m_t and m_h):
+        return None
+    h = hashlib.sha256()
+    for f in ("la_fwd_bf16.hip", "la_common.h"):
+        with open(os.path.join(ROOT, "hybrid_linear_attention_lightning_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return int(m_t.group(1)) if h.hexdigest() == m_h.group(1) else None
+
+
 def prefill_counts(B, H, N, d, C):
     """Algorithmic bytes and flops of one forward pass (q, k, v read, o
     written, final state written; causal intra-chunk products counted once)."""
@@ -103,7 +125,7 @@ def bench_prefill(args, torch, la, la_inputs):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(),
             "bytes_per_launch": bytes_,
         },
         "mfma": {

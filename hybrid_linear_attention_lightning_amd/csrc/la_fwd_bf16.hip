@@ -215,25 +215,29 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) offV[ct][hh] = off_tr(hh, 2 * wave + ct);
   }
-  // The per-lane offsets are re-issued at the top of every chunk through an
-  // empty asm, so the compiler cannot hoist the dozens of addresses derived
-  // from them out of the chunk loop, where they would stay live and spill.
-  int lA[G::KSD], lC[G::KSD][2], lT[G::NT][2], lV[CT][2];
+  // The per-lane offsets are re-issued in place at the top of every chunk
+  // through an empty asm, so the compiler cannot hoist the dozens of
+  // addresses derived from them out of the chunk loop, where they would stay
+  // live and spill.
   auto refresh_offsets = [&]() {
 #pragma unroll
     for (int ks = 0; ks < G::KSD; ++ks) {
-      lA[ks] = opaque(offA[ks]);
-      lC[ks][0] = opaque(offC[ks][0]);
-      lC[ks][1] = opaque(offC[ks][1]);
+      offA[ks] = opaque(offA[ks]);
+      offC[ks][0] = opaque(offC[ks][0]);
+      offC[ks][1] = opaque(offC[ks][1]);
     }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-      for (int t = 0; t < G::NT; ++t) lT[t][hh] = opaque(offT[t][hh]);
+      for (int t = 0; t < G::NT; ++t) offT[t][hh] = opaque(offT[t][hh]);
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) lV[ct][hh] = opaque(offV[ct][hh]);
+      for (int ct = 0; ct < CT; ++ct) offV[ct][hh] = opaque(offV[ct][hh]);
     }
   };
+  auto& lA = offA;
+  auto& lC = offC;
+  auto& lT = offT;
+  auto& lV = offV;
 
   // column fragment: 8 tokens 32ks + 8lg .. +7 of one column, from two
   // transposing reads
