@@ -30,6 +30,10 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
     # packed fp32 instructions stay off: plain float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs: the prefill kernel scales and
+    # packs its accumulators on the vector ALU, and accumulators placed in
+    # AGPRs cost a copy in and out for each such access (measured ~4% faster)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE,
 ]
 

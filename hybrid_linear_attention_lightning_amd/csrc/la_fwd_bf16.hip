@@ -272,18 +272,20 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
     const uint16_t* base = src + (long)(reverse ? (N - tc - n) : tc) * D;
     const uint32_t lds0 = opaque_s((uint32_t)(uintptr_t)(tile + G::RPI * wave * D));
     constexpr uint32_t kMoveBytes = 2u * G::RPI * G::NW * D;  // LDS bytes between moves
+    // offsets are unsigned 32-bit, so the loads take the scalar-base +
+    // 32-bit vector-offset form
     if (n == C) {
 #pragma unroll
       for (int m = 0; m < DM_N; ++m)
         __builtin_amdgcn_global_load_lds(
-            base + (dm_off + m * dm_step),
+            base + (uint32_t)(dm_off + m * dm_step),
             (__attribute__((address_space(3))) void*)(uintptr_t)(lds0 + kMoveBytes * m), 16, 0, 0);
     } else {
 #pragma unroll
       for (int m = 0; m < DM_N; ++m) {
         const int rr = min(dm_row0 + DM_STEP * m, n - 1);
         __builtin_amdgcn_global_load_lds(
-            base + ((reverse ? (n - 1 - rr) : rr) * D + dm_col),
+            base + (uint32_t)((reverse ? (n - 1 - rr) : rr) * D + dm_col),
             (__attribute__((address_space(3))) void*)(uintptr_t)(lds0 + kMoveBytes * m), 16, 0, 0);
       }
     }
@@ -584,13 +586,15 @@ hipError_t launch_fwd_bf16(const FwdPass& p, hipStream_t s) {
 }
 
 hipError_t launch_pieces_bf16(const PiecePass& p, hipStream_t s) {
+  // A piece state does not depend on the chunk length it is accumulated in,
+  // and piece lengths are multiples of C.  Chunks of at most 64 tokens keep
+  // the double-buffered K and V tiles at 64 KB (d = 128), so two workgroups
+  // share a CU and hide each other's load latency.
   if (p.D == 128) {
-    if (p.C == 128) return launch_pieces_cd<128, 128>(p, s);
-    if (p.C == 64) return launch_pieces_cd<64, 128>(p, s);
+    if (p.C >= 64) return launch_pieces_cd<64, 128>(p, s);
     if (p.C == 32) return launch_pieces_cd<32, 128>(p, s);
   } else if (p.D == 64) {
-    if (p.C == 128) return launch_pieces_cd<128, 64>(p, s);
-    if (p.C == 64) return launch_pieces_cd<64, 64>(p, s);
+    if (p.C >= 64) return launch_pieces_cd<64, 64>(p, s);
     if (p.C == 32) return launch_pieces_cd<32, 64>(p, s);
   }
   return hipErrorInvalidValue;
