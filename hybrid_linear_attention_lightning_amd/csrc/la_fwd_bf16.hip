@@ -159,7 +159,11 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
   const float sl2 = slope[bh % H] * kLog2e;  // lambda^e = exp2(-sl2 * e)
   const int col0 = 32 * wave;                // this wave's first value column
 
-  // ---- fp32 state: S[t][ct][r] = S[feature 16t + 4lg + r][value col0 + 16ct + li]
+  // ---- fp32 state: S[t][ct][r] = S[feature feat(t, r)][value col0 + 16ct + li]
+  // Feature order: tiles 2m and 2m+1 hold, in lane group lg, the two halves
+  // of the 8 consecutive features 32m + 8lg .. +7, so that the state, split
+  // into bf16 operands, meets Q in the plain row-fragment order.
+  auto feat = [&](int t, int r) { return 32 * (t >> 1) + 8 * lg + 4 * (t & 1) + r; };
   f32x4_t S[G::NT][CT];
 #pragma unroll
   for (int t = 0; t < G::NT; ++t)
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        S[t][ct][r] = s_init ? s_init[(size_t)(16 * t + 4 * lg + r) * D + col0 + 16 * ct + li] : 0.f;
+        S[t][ct][r] = s_init ? s_init[(size_t)feat(t, r) * D + col0 + 16 * ct + li] : 0.f;
 
   // ---- per-lane decay tables --------------------------------------------
   // P^T tile element: key row 16kb + 4lg + r, query column 16qb + li.
@@ -194,26 +198,23 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
   int offA[G::KSD];
 #pragma unroll
   for (int ks = 0; ks < G::KSD; ++ks) offA[ks] = li * D + 8 * ((4 * ks + lg) ^ sA);
-  // permuted Q fragments (2 x 8 B): row 16qb + li, features 32ks + 16hh + 4lg .. +3
-  int offC[G::KSD][2];
-#pragma unroll
-  for (int ks = 0; ks < G::KSD; ++ks)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-      offC[ks][hh] = li * D + 8 * ((4 * ks + (lg >> 1) + 2 * hh) ^ sA) + 4 * (lg & 1);
-  // transposing reads: row 8lg + (li>>2) + 4hh (+32ks), columns 16t + 4(li&3) .. +3;
-  // the lane group's lane i then receives column 16t + i of those 4 rows
-  auto off_tr = [&](int hh, int t) {
+  // transposing reads: row 8lg + (li>>2) + 4hh (+32ks), 4 columns from
+  // cols(li&3) on; lane i of the lane group then receives column
+  // cols(i>>2) + (i&3) of those 4 rows.  Value tiles take the columns in
+  // order (cols(j) = 16ct + 4j), K^T tiles in the state's feature order
+  // (cols(j) = feat(t, 0) of lane group j).
+  auto off_tr = [&](int hh, int chunk16, int half) {
     const int r = 8 * lg + (li >> 2) + 4 * hh;
-    return r * D + 8 * ((2 * t + ((li & 3) >> 1)) ^ swz_of<D>(r & 15)) + 4 * (li & 1);
+    return r * D + 8 * (chunk16 ^ swz_of<D>(r & 15)) + 4 * half;
   };
   int offT[G::NT][2], offV[CT][2];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-    for (int t = 0; t < G::NT; ++t) offT[t][hh] = off_tr(hh, t);
+    for (int t = 0; t < G::NT; ++t) offT[t][hh] = off_tr(hh, 4 * (t >> 1) + (li & 3), t & 1);
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) offV[ct][hh] = off_tr(hh, 2 * wave + ct);
+    for (int ct = 0; ct < CT; ++ct)
+      offV[ct][hh] = off_tr(hh, 2 * (2 * wave + ct) + ((li & 3) >> 1), li & 1);
   }
   // The per-lane offsets are re-issued in place at the top of every chunk
   // through an empty asm, so the compiler cannot hoist the dozens of
@@ -223,8 +224,6 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
 #pragma unroll
     for (int ks = 0; ks < G::KSD; ++ks) {
       offA[ks] = opaque(offA[ks]);
-      offC[ks][0] = opaque(offC[ks][0]);
-      offC[ks][1] = opaque(offC[ks][1]);
     }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -235,7 +234,6 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
     }
   };
   auto& lA = offA;
-  auto& lC = offC;
   auto& lT = offT;
   auto& lV = offV;
 
@@ -300,7 +298,78 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
   };
 
   // S <- lambda^n S + K^T diag(b) V for the chunk (K tile Kt, V fragments vf)
-  auto state_update = [&](const uint16_t* Kt, const u32x4_t (&vf)[G::KSC][CT], int n) {
+  // FULL (n == C) is a compile-time flag, so that a full chunk's update is
+  // one branch-free block the scheduler can interleave across token steps.
+  // b*V for token step ks as hi/lo B operands: unit u = (ct, c) covers 4 of
+  // the 8 tokens of one value tile
+  auto make_bv_unit = [&](const u32x4_t (&vf)[G::KSC][CT], int ks, const float (&bk)[8], int u,
+                          u32x4_t (&bvh)[CT], u32x4_t (&bvl)[CT]) __attribute__((always_inline)) {
+    const int ct = u >> 1, c = u & 1;
+    const uint32_t w0 = vf[ks][ct][2 * c], w1 = vf[ks][ct][2 * c + 1];
+    const f32x4_t x = {bf_lo(w0) * bk[4 * c], bf_hi(w0) * bk[4 * c + 1],
+                       bf_lo(w1) * bk[4 * c + 2], bf_hi(w1) * bk[4 * c + 3]};
+    u32x2_t h2, l2;
+    split4(x, h2, l2);
+    bvh[ct][2 * c] = h2[0];
+    bvh[ct][2 * c + 1] = h2[1];
+    bvl[ct][2 * c] = l2[0];
+    bvl[ct][2 * c + 1] = l2[1];
+  };
+  // S <- lambda^n S + K^T diag(b) V for the chunk (K tile Kt, V fragments vf).
+  // A full chunk's update is scheduled by hand: 32 groups (token step ks,
+  // state tile t) of four products, each carrying a slice of the vector work
+  // of the next step's b*V and the K^T reads three groups ahead, closed by a
+  // scheduling fence.  A single wave then keeps the matrix cores and the
+  // vector ALU busy together, which the compiler's own order does not.
+  auto state_update_full = [&](const uint16_t* Kt, const u32x4_t (&vf)[G::KSC][CT]) __attribute__((always_inline)) {
+    constexpr int NG = G::KSC * G::NT;  // groups
+    constexpr int PF = 3;               // K^T prefetch distance (groups)
+    const float gdec = fast_exp2(-sl2 * (float)C);
+    float bk[8];
+    auto set_bk = [&](int ks) {
+      const float f = fast_exp2(-sl2 * (float)(32 * (G::KSC - 1 - ks)));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bk[e] = f * bl[e];
+    };
+    u32x4_t bvh[2][CT], bvl[2][CT];
+    set_bk(0);
+#pragma unroll
+    for (int u = 0; u < 2 * CT; ++u) make_bv_unit(vf, 0, bk, u, bvh[0], bvl[0]);
+    u32x4_t kt[PF + 1];
+#pragma unroll
+    for (int g = 0; g < PF; ++g) kt[g] = col_frag(Kt, g / G::NT, lT[g % G::NT]);
+    if (G::KSC > 1) set_bk(1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int ks = g / G::NT, t = g % G::NT;
+      if (g + PF < NG) kt[(g + PF) % (PF + 1)] = col_frag(Kt, (g + PF) / G::NT, lT[(g + PF) % G::NT]);
+      if (ks == 0) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S[t][ct][r] *= gdec;
+      }
+      const u32x4_t& k = kt[g % (PF + 1)];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) S[t][ct] = mfma16(k, bvh[ks & 1][ct], S[t][ct]);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) S[t][ct] = mfma16(k, bvl[ks & 1][ct], S[t][ct]);
+      // vector work of step ks+1: its 2*CT b*V units spread evenly over the
+      // step's NT groups, then the b factors of step ks+2
+      if (ks + 1 < G::KSC) {
+        constexpr int US = G::NT / (2 * CT);  // groups per unit
+        static_assert(US >= 1 && G::NT % (2 * CT) == 0, "b*V units per step");
+        if (t % US == US - 1)
+          make_bv_unit(vf, ks + 1, bk, t / US, bvh[(ks + 1) & 1], bvl[(ks + 1) & 1]);
+        if (t == G::NT - 1 && ks + 2 < G::KSC) set_bk(ks + 2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // compiler-scheduled order: partial chunks (the last of a sequence) and the
+  // piece kernel
+  auto state_update_partial = [&](const uint16_t* Kt, const u32x4_t (&vf)[G::KSC][CT], int n) __attribute__((always_inline)) {
     const float gdec = fast_exp2(-sl2 * (float)n);
 #pragma unroll
     for (int t = 0; t < G::NT; ++t)
@@ -324,20 +393,7 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
       }
       u32x4_t bvh[CT], bvl[CT];
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const uint32_t w0 = vf[ks][ct][2 * c], w1 = vf[ks][ct][2 * c + 1];
-          const f32x4_t x = {bf_lo(w0) * bk[4 * c], bf_hi(w0) * bk[4 * c + 1],
-                             bf_lo(w1) * bk[4 * c + 2], bf_hi(w1) * bk[4 * c + 3]};
-          u32x2_t h2, l2;
-          split4(x, h2, l2);
-          bvh[ct][2 * c] = h2[0];
-          bvh[ct][2 * c + 1] = h2[1];
-          bvl[ct][2 * c] = l2[0];
-          bvl[ct][2 * c + 1] = l2[1];
-        }
-      }
+      for (int u = 0; u < 2 * CT; ++u) make_bv_unit(vf, ks, bk, u, bvh, bvl);
 #pragma unroll
       for (int t = 0; t < G::NT; ++t) {
         const u32x4_t kt = col_frag(Kt, ks, lT[t]);
@@ -347,6 +403,14 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
         for (int ct = 0; ct < CT; ++ct) S[t][ct] = mfma16(kt, bvl[ct], S[t][ct]);
       }
     }
+  };
+  auto state_update = [&](const uint16_t* Kt, const u32x4_t (&vf)[G::KSC][CT], int n) __attribute__((always_inline)) {
+    // The piece kernel keeps the compiler-scheduled loop: the hand
+    // schedule's extra live fragments would halve its occupancy.
+    if (!STATE_ONLY && n == C)
+      state_update_full(Kt, vf);
+    else
+      state_update_partial(Kt, vf, n);
   };
 
   if constexpr (STATE_ONLY) {
@@ -469,7 +533,7 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
       }
 
       // S_{c-1} as hi/lo bf16 A operands of S^T (value row li, features
-      // {32ks + 4lg + r} and {32ks + 16 + 4lg + r})
+      // 32ks + 8lg .. +7)
       u32x4_t sfh[CT][G::KSD], sfl[CT][G::KSD];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
@@ -497,48 +561,52 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
       const int li_c = opaque(li);
       const int o_lane = 4 * lg + (reverse ? (n - 1 - li_c) : li_c) * D;
       const int o_qb = reverse ? -16 * D : 16 * D;
+      // a full chunk stores every row: its output loop has no branches
+      auto outputs = [&](auto full_c) {
+        constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
-      for (int qb = 0; qb < G::NQB; ++qb) {
-        // Q^T as B operand in the feature order of the S fragments
-        u32x4_t qf[G::KSD];
+        for (int qb = 0; qb < G::NQB; ++qb) {
+          // Q^T as B operand: row fragments, the S fragments' feature order
+          u32x4_t qf[G::KSD];
 #pragma unroll
-        for (int ks = 0; ks < G::KSD; ++ks) {
-          const u32x2_t a0 = lds_read8(Qs + 16 * qb * D + lC[ks][0]);
-          const u32x2_t a1 = lds_read8(Qs + 16 * qb * D + lC[ks][1]);
-          qf[ks] = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
-        }
-        u32x4_t pfh[G::KSC], pfl[G::KSC];
-#pragma unroll
-        for (int ks = 0; ks <= qb / 2; ++ks) {
-          pfh[ks] = lds_read16(Pth + (frag_base(qb) + ks) * 512 + 8 * lane);
-          pfl[ks] = lds_read16(Ptl + (frag_base(qb) + ks) * 512 + 8 * lane);
-        }
-        const float aq = a_lane * fast_exp2(-sl2 * (float)(16 * qb));
-        f32x4_t acc[CT];
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          f32x4_t x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < G::KSD; ++ks) {
-            x = mfma16(sfh[ct][ks], qf[ks], x);
-            x = mfma16(sfl[ct][ks], qf[ks], x);
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[ct][r] = x[r] * aq;
+          for (int ks = 0; ks < G::KSD; ++ks) qf[ks] = lds_read16(Qs + 16 * qb * D + lA[ks]);
+          u32x4_t pfh[G::KSC], pfl[G::KSC];
 #pragma unroll
           for (int ks = 0; ks <= qb / 2; ++ks) {
-            acc[ct] = mfma16(vf[ks][ct], pfh[ks], acc[ct]);
-            acc[ct] = mfma16(vf[ks][ct], pfl[ks], acc[ct]);
+            pfh[ks] = lds_read16(Pth + (frag_base(qb) + ks) * 512 + 8 * lane);
+            pfl[ks] = lds_read16(Ptl + (frag_base(qb) + ks) * 512 + 8 * lane);
+          }
+          const float aq = a_lane * fast_exp2(-sl2 * (float)(16 * qb));
+          f32x4_t acc[CT];
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < G::KSD; ++ks) {
+              x = mfma16(sfh[ct][ks], qf[ks], x);
+              x = mfma16(sfl[ct][ks], qf[ks], x);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[ct][r] = x[r] * aq;
+#pragma unroll
+            for (int ks = 0; ks <= qb / 2; ++ks) {
+              acc[ct] = mfma16(vf[ks][ct], pfh[ks], acc[ct]);
+              acc[ct] = mfma16(vf[ks][ct], pfl[ks], acc[ct]);
+            }
+          }
+          if (FULL || 16 * qb + li_c < n) {
+            uint16_t* dst = obase + (o_lane + qb * o_qb);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+              *reinterpret_cast<u32x2_t*>(dst + 16 * ct) =
+                  u32x2_t{pack2(acc[ct][0], acc[ct][1]), pack2(acc[ct][2], acc[ct][3])};
           }
         }
-        if (16 * qb + li_c < n) {
-          uint16_t* dst = obase + (o_lane + qb * o_qb);
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct)
-            *reinterpret_cast<u32x2_t*>(dst + 16 * ct) =
-                u32x2_t{pack2(acc[ct][0], acc[ct][1]), pack2(acc[ct][2], acc[ct][3])};
-        }
-      }
+      };
+      if (n == C)
+        outputs(std::true_type{});
+      else
+        outputs(std::false_type{});
       lds_barrier();  // Q and P^T tiles are free for the next chunk
     }
   }
@@ -550,7 +618,7 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          s_final[(size_t)(16 * t + 4 * lg + r) * D + col0 + 16 * ct + li] = S[t][ct][r];
+          s_final[(size_t)feat(t, r) * D + col0 + 16 * ct + li] = S[t][ct][r];
   }
 }
 
