@@ -72,6 +72,15 @@ __device__ __forceinline__ u32x2_t lds_read_tr8(const uint16_t* p) {
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
 // operations, not for its outstanding global loads (which may be prefetching
 // the next chunk, directly into LDS or into registers).
+// Wait until at most N vector-memory operations of this wave are
+// outstanding (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt
+// and lgkmcnt left at their maxima, i.e. not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }

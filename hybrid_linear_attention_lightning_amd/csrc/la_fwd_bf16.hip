@@ -37,8 +37,8 @@
 //    depends only on the row modulo 16, so every LDS address is a per-lane
 //    constant plus a compile-time offset; K^T and V^T fragments (contractions
 //    over tokens) come straight from the row-major tiles through the
-//    transposing LDS read of gfx950; K and V move global -> LDS without
-//    registers, Q goes global -> registers one chunk ahead.
+//    transposing LDS read of gfx950; Q, K and V move global -> LDS without
+//    passing through registers.
 // The same kernel in STATE_ONLY mode computes piece states (K^T diag(b) V
 // accumulated over a piece) for the segment pre-pass.
 #include <type_traits>
@@ -67,13 +67,11 @@ struct Cfg {
   static constexpr int NFRAG = frag_base(NQB);
   static constexpr int CPR = D / 8;    // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR; // rows per wave-wide 16-byte-per-lane move
-  static constexpr int QCH = C * CPR / THREADS;   // Q chunks per thread
   static constexpr int TILE = C * D;              // elements per tile
   static constexpr int PT_HALF = NFRAG * 64 * 8;  // one of P_hi / P_lo
   static_assert(C == 32 || C == 64 || C == 128, "chunk");
   static_assert(D == 64 || D == 128, "head dim");
-  static_assert(QCH >= 1, "tile smaller than one chunk per thread");
-  static_assert((RPI * NW) % 16 == 0 && (THREADS / CPR) % 16 == 0, "row mod 16 per lane");
+  static_assert((RPI * NW) % 16 == 0, "row mod 16 per lane");
   static_assert(C % (RPI * NW) == 0, "whole direct moves per wave");
   static_assert((STATE_ONLY ? 4 * TILE : 3 * TILE + 2 * PT_HALF) * 2 <= 160 * 1024, "LDS");
 };
@@ -444,38 +442,48 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
   } else {
     __shared__ __attribute__((aligned(16))) uint16_t Ks[G::TILE], Vs[G::TILE], Qs[G::TILE],
         Pth[G::PT_HALF], Ptl[G::PT_HALF];
-    // Q: thread chunk m is row tid/CPR + (THREADS/CPR) m, chunk tid % CPR
-    const int qrow = tid / G::CPR;
-    const int qoff = qrow * D + 8 * ((tid % G::CPR) ^ swz_of<D>(qrow & 15));
-    u32x4_t qstg[G::QCH];
-    auto load_q = [&](int tc, int n) {
-      const uint16_t* base = qg + (long)(reverse ? (N - tc - n) : tc) * D + 8 * (tid % G::CPR);
-#pragma unroll
-      for (int m = 0; m < G::QCH; ++m) {
-        const int rr = min(qrow + (kThreads / G::CPR) * m, n - 1);
-        qstg[m] = *reinterpret_cast<const u32x4_t*>(base + (reverse ? (n - 1 - rr) : rr) * D);
-      }
-    };
+    // All three tiles move straight from HBM to LDS.  Per chunk: K and V
+    // (issued during the previous chunk's outputs) feed the state update,
+    // which gives Q (issued last, once the previous outputs are done with
+    // its tile) time to land before the score tiles need it.
     if (tau0 < tau_end) {
       const int n0 = min(C, tau_end - tau0);
       load_direct(kg, Ks, tau0, n0);
       load_direct(vg, Vs, tau0, n0);
-      load_q(tau0, n0);
+      load_direct(qg, Qs, tau0, n0);
     }
     for (int tc = tau0; tc < tau_end; tc += C) {
       const int n = min(C, tau_end - tc);
       const bool more = tc + C < tau_end;
       const int n_next = more ? min(C, tau_end - tc - C) : 0;
       refresh_offsets();
-#pragma unroll
-      for (int m = 0; m < G::QCH; ++m)
-        *reinterpret_cast<u32x4_t*>(Qs + qoff + (kThreads / G::CPR) * m * D) = qstg[m];
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's K/V loads have landed
-      lds_barrier();                  // chunk tc is in LDS
-      if (more) load_q(tc + C, n_next);
+      // Vector-memory operations complete in issue order: with at most
+      // DM_N (Q's moves) outstanding, this wave's K and V moves and earlier
+      // output stores are done.
+      wait_vmcnt<DM_N>();
+      lds_barrier();  // K and V of chunk tc are in LDS
 
       u32x4_t vf[G::KSC][CT];
       load_vfr(Vs, vf);
+
+      // S_{c-1} as hi/lo bf16 A operands of S^T (value row li, features
+      // 32ks + 8lg .. +7)
+      u32x4_t sfh[CT][G::KSD], sfl[CT][G::KSD];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int ks = 0; ks < G::KSD; ++ks) {
+          u32x2_t h0, l0, h1, l1;
+          split4(S[2 * ks][ct], h0, l0);
+          split4(S[2 * ks + 1][ct], h1, l1);
+          sfh[ct][ks] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
+          sfl[ct][ks] = u32x4_t{l0[0], l0[1], l1[0], l1[1]};
+        }
+
+      state_update(Ks, vf, n);
+
+      wait_vmcnt<0>();
+      lds_barrier();  // Q of chunk tc is in LDS
 
       // ---- masked scores P^T = (K Q^T) * M^T -> LDS as hi/lo B fragments ----
       // Tile (kb, qb), lane (lg, li) holds keys 16kb + 4lg + r of query
@@ -531,22 +539,6 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
         if constexpr (G::NPAIR > 2) if (pr == 2) pair_tiles(std::integral_constant<int, 2>{});
         if constexpr (G::NPAIR > 3) if (pr == 3) pair_tiles(std::integral_constant<int, 3>{});
       }
-
-      // S_{c-1} as hi/lo bf16 A operands of S^T (value row li, features
-      // 32ks + 8lg .. +7)
-      u32x4_t sfh[CT][G::KSD], sfl[CT][G::KSD];
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int ks = 0; ks < G::KSD; ++ks) {
-          u32x2_t h0, l0, h1, l1;
-          split4(S[2 * ks][ct], h0, l0);
-          split4(S[2 * ks + 1][ct], h1, l1);
-          sfh[ct][ks] = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
-          sfl[ct][ks] = u32x4_t{l0[0], l0[1], l1[0], l1[1]};
-        }
-
-      state_update(Ks, vf, n);
 
       lds_barrier();  // P^T fragments written; K and V tiles are dead
       if (more) {
@@ -608,6 +600,7 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
       else
         outputs(std::false_type{});
       lds_barrier();  // Q and P^T tiles are free for the next chunk
+      if (more) load_direct(qg, Qs, tc + C, n_next);
     }
   }
 
