@@ -77,10 +77,11 @@ struct Cfg {
 };
 
 // Swizzle of the 16-byte chunk index of row r of a [C][D] bf16 tile.  It
-// depends on r mod 16 only, and makes the row-fragment reads (16 rows x 16 B),
-// the permuted 8-byte Q reads, the transposing reads (4 rows x 32 B per lane
-// group) and the 16-byte staging writes free of LDS bank conflicts (checked
-// against a 64-bank model for every pattern the kernel issues).
+// depends on r mod 16 only.  In a 64-bank model with 16 lanes served per
+// pass, it keeps the row-fragment reads (16 rows x 16 B), the transposing
+// reads and the 16-byte direct moves free of bank conflicts at D = 128; the
+// K^T read in the state's feature order touches one 8-byte half of each
+// chunk and is 2-way at D = 64.
 template <int D>
 __host__ __device__ constexpr int swz_of(int r) {
   if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
