@@ -33,11 +33,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_code_digest():
+    """sha256 of the main prefill kernel's code: its two source files with
+    // comments, indentation and blank lines removed, so that edits to
+    comments alone do not invalidate counters taken on the same code."""
+    import hashlib
+    import re
+
+    h = hashlib.sha256()
+    for f in ("la_fwd_bf16.hip", "la_common.h"):
+        with open(os.path.join(ROOT, "hybrid_linear_attention_lightning_amd", "csrc", f)) as fh:
+            for line in fh:
+                code = re.sub(r"//.*", "", line).strip()
+                if code:
+                    h.update(code.encode() + b"\n")
+    return h.hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per launch of the main prefill kernel from the committed
-    FETCH_SIZE / WRITE_SIZE summary, or None when the kernel source has
-    changed since those counters were taken (its sha256 no longer matches)."""
-    import hashlib
+    FETCH_SIZE / WRITE_SIZE summary, or None when the kernel code has
+    changed since those counters were taken (its digest no longer matches)."""
     import re
 
     path = os.path.join(ROOT, "profiles", "prefill_128k_hbm_traffic.md")
@@ -45,14 +61,10 @@ def measured_traffic():
         return None
     text = open(path).read()
     m_t = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
-    m_h = re.search(r"^kernel_source_sha256: ([0-9a-f]{64})$", text, re.M)
+    m_h = re.search(r"^kernel_code_sha256: ([0-9a-f]{64})$", text, re.M)
     if not (m_t and m_h):
         return None
-    h = hashlib.sha256()
-    for f in ("la_fwd_bf16.hip", "la_common.h"):
-        with open(os.path.join(ROOT, "hybrid_linear_attention_lightning_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return int(m_t.group(1)) if h.hexdigest() == m_h.group(1) else None
+    return int(m_t.group(1)) if kernel_code_digest() == m_h.group(1) else None
 
 
 def prefill_counts(B, H, N, d, C):
