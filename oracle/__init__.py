@@ -10,15 +10,18 @@ lambda = exp(-slope), Ling & Ring 2.6 Technical Report pages, "Hybrid Linear
 Attention" and "Context Parallel for Lightning Attention" sections):
 
 * `fwd`, `decode`, `bwd`, `fwd_chunked` call the plain C recurrent code in
-  `la_oracle.c` (fp64, OpenMP over (b, h));
+  `la_oracle.c` (fp64, OpenMP over (b, h)); `fwd_varlen` and `bwd_varlen`
+  apply them to each sequence of a packed batch;
 * `brute` holds the quadratic (masked-matrix) forms in numpy, for tiny sizes.
 """
 from .core import (  # noqa: F401
     build,
     fwd,
     fwd_chunked,
+    fwd_varlen,
     decode,
     bwd,
+    bwd_varlen,
     num_threads,
     library_path,
 )

@@ -123,3 +123,49 @@ def bwd(q, k, v, dout, slope, S0=None):
         B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s), _ptr(S0), _ptr(dq), _ptr(dk), _ptr(dv)
     )
     return dq, dk, dv
+
+
+def _check_cu(cu, T):
+    cu = [int(x) for x in cu]
+    assert len(cu) >= 2 and cu[0] == 0 and cu[-1] == T, "cu_seqlens must run from 0 to T"
+    assert all(a <= b for a, b in zip(cu, cu[1:])), "cu_seqlens must be non-decreasing"
+    return cu
+
+
+def fwd_varlen(q, k, v, slope, cu_seqlens, S0=None):
+    """Packed sequences.  q, k, v: [H,T,d]; sequence s holds tokens
+    cu_seqlens[s] .. cu_seqlens[s+1]-1 of every head; S0: [nseq,H,d,d] or None.
+
+    Every sequence is its own recurrence from its own initial state (the
+    varlen batches of the "Context Parallel for Lightning Attention" section,
+    and prefix caching on the "linghe" section: a cached state continues a
+    sequence).  Returns (o [H,T,d], S [nseq,H,d,d]) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    H, T, d = q.shape
+    cu = _check_cu(cu_seqlens, T)
+    nseq = len(cu) - 1
+    o = np.empty_like(q)
+    S = np.empty((nseq, H, d, d), dtype=np.float64)
+    for s in range(nseq):
+        a, b = cu[s], cu[s + 1]
+        init = None if S0 is None else _f64(S0)[s][None]
+        o_s, S_s = fwd(q[None, :, a:b], k[None, :, a:b], v[None, :, a:b], slope, init)
+        o[:, a:b] = o_s[0]
+        S[s] = S_s[0]
+    return o, S
+
+
+def bwd_varlen(q, k, v, dout, slope, cu_seqlens):
+    """Gradients (dq, dk, dv) [H,T,d] of L = sum(o * dout) for packed
+    sequences with zero initial states."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+    H, T, d = q.shape
+    cu = _check_cu(cu_seqlens, T)
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        if a == b:
+            continue
+        r = bwd(q[None, :, a:b], k[None, :, a:b], v[None, :, a:b], g[None, :, a:b], slope)
+        dq[:, a:b], dk[:, a:b], dv[:, a:b] = (x[0] for x in r)
+    return dq, dk, dv

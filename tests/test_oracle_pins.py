@@ -5,7 +5,10 @@ oracle is pinned by mathematics: a worked example derived by hand from the
 definition, the quadratic (masked-matrix) form, closed-form special cases,
 linearity, continuation of the state, the context-parallel state algebra the
 pages describe ("Context Parallel for Lightning Attention": local recursion plus
-a global correction) and central finite differences for the backward.
+a global correction) and central finite differences for the backward.  Packed
+(varlen) batches are pinned to the block-diagonal masked-matrix form, to
+prefix caching (continuing from a cached state) and to the independence of
+the sequences.
 """
 import numpy as np
 import pytest
@@ -217,6 +220,105 @@ def test_context_parallel_state_algebra(oracle_mod, bounds):
         corr = fac[..., None] * np.einsum("bhti,bhij->bhtj", q[:, :, a:b], S_in)
         corrected.append(locs[r][0] + corr)
     assert _relerr(np.concatenate(corrected, axis=2), o) < 1e-12
+
+
+# ------------------------------------------------------------ packed sequences
+_CU_CASES = [(0, 7, 7, 8, 30, 61), (0, 61), (0, 1, 2, 3), (0, 0, 20)]
+
+
+def _packed(seed, H, T, d):
+    rng = _rng(seed)
+    return tuple(_rand(rng, H, T, d) for _ in range(3))
+
+
+@pytest.mark.parametrize("cu", _CU_CASES)
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_varlen_matches_packed_quadratic_form(oracle_mod, cu, with_s0):
+    """Recurrence per sequence against the block-diagonal masked-matrix form."""
+    H, d = 2, 5
+    q, k, v = _packed(30, H, cu[-1], d)
+    S0 = _rand(_rng(31), len(cu) - 1, H, d, d) if with_s0 else None
+    s = np.array([0.05, 0.9], dtype=np.float32)
+    o, S = oracle_mod.fwd_varlen(q, k, v, s, cu, S0)
+    ob, Sb = oracle_mod.brute.fwd_varlen(q, k, v, s, cu, S0)
+    assert _relerr(o, ob) < 1e-12 and _relerr(S, Sb) < 1e-12
+
+
+def test_packed_quadratic_form_with_one_sequence_is_the_plain_form(oracle_mod):
+    H, T, d = 3, 19, 4
+    q, k, v = _packed(32, H, T, d)
+    S0 = _rand(_rng(33), 1, H, d, d)
+    s = np.array([0.0, 0.2, 2.0], dtype=np.float32)
+    o, S = oracle_mod.brute.fwd_varlen(q, k, v, s, (0, T), S0)
+    op, Sp = oracle_mod.brute.fwd(q[None], k[None], v[None], s, S0)
+    assert _relerr(o, op[0]) < 1e-13 and _relerr(S, Sp) < 1e-13
+
+
+def test_varlen_prefix_caching(oracle_mod):
+    """A sequence continued from the cached state of its prefix gives the
+    outputs and final state of the whole sequence."""
+    H, T, m, d = 2, 45, 17, 6
+    q, k, v = _packed(34, H, T, d)
+    S0 = _rand(_rng(35), 1, H, d, d, scale=0.3)
+    s = np.array([0.01, 0.4], dtype=np.float32)
+    o, S = oracle_mod.fwd_varlen(q, k, v, s, (0, T), S0)
+    o1, S1 = oracle_mod.fwd_varlen(q[:, :m], k[:, :m], v[:, :m], s, (0, m), S0)
+    o2, S2 = oracle_mod.fwd_varlen(q[:, m:], k[:, m:], v[:, m:], s, (0, T - m), S1)
+    assert _relerr(np.concatenate([o1, o2], axis=1), o) < 1e-13
+    assert _relerr(S2, S) < 1e-13
+
+
+def test_varlen_sequences_are_independent(oracle_mod):
+    cu = (0, 11, 11, 30, 42)
+    H, d = 2, 4
+    q, k, v = _packed(36, H, cu[-1], d)
+    s = np.array([0.0, 0.3], dtype=np.float32)
+    o, S = oracle_mod.fwd_varlen(q, k, v, s, cu)
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    for x in (q2, k2, v2):
+        x[:, 11:30] += 1.0  # sequence 2 only
+    o2, S2 = oracle_mod.fwd_varlen(q2, k2, v2, s, cu)
+    keep = np.r_[0:11, 30:42]
+    assert np.array_equal(o[:, keep], o2[:, keep])
+    assert np.array_equal(S[[0, 1, 3]], S2[[0, 1, 3]])
+    assert not np.allclose(o[:, 11:30], o2[:, 11:30])
+    # the empty sequence passes its (zero) initial state through
+    assert np.array_equal(S[1], np.zeros_like(S[1]))
+
+
+@pytest.mark.parametrize("cu", _CU_CASES)
+def test_varlen_backward_matches_packed_quadratic_form(oracle_mod, cu):
+    H, d = 2, 5
+    q, k, v = _packed(37, H, cu[-1], d)
+    g = _rand(_rng(38), H, cu[-1], d)
+    s = np.array([0.05, 0.9], dtype=np.float32)
+    got = oracle_mod.bwd_varlen(q, k, v, g, s, cu)
+    ref = oracle_mod.brute.bwd_varlen(q, k, v, g, s, cu)
+    for a, b in zip(got, ref):
+        if b.size:
+            assert _relerr(a, b) < 1e-12
+
+
+def test_varlen_backward_finite_differences(oracle_mod):
+    """Central differences of L = sum(o * dO) through the packed forward."""
+    cu = (0, 9, 10, 33)
+    H, d = 2, 4
+    q, k, v = _packed(39, H, cu[-1], d)
+    g = _rand(_rng(40), H, cu[-1], d)
+    s = np.array([0.1, 0.7], dtype=np.float32)
+    grads = oracle_mod.bwd_varlen(q, k, v, g, s, cu)
+    eps = 1e-6
+    rng = _rng(41)
+    for which in range(3):
+        for _ in range(40):
+            ix = tuple(rng.integers(0, n) for n in q.shape)
+            xs = [q.copy(), k.copy(), v.copy()]
+            xs[which][ix] += eps
+            lp = np.sum(oracle_mod.fwd_varlen(*xs, s, cu)[0] * g)
+            xs[which][ix] -= 2 * eps
+            lm = np.sum(oracle_mod.fwd_varlen(*xs, s, cu)[0] * g)
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - grads[which][ix]) < 1e-6 * max(1.0, np.max(np.abs(grads[which])))
 
 
 # ---------------------------------------------------------------------- backward
