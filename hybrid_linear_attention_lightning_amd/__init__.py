@@ -9,6 +9,7 @@ for device memory (tensors) and streams.
     o, S = prefill(q, k, v, slope, chunk=128)        # q, k, v: [B, H, N, d] cuda tensors
     o    = decode_step(q1, k1, v1, slope, S)          # S updated in place
     dq, dk, dv = prefill_bwd(q, k, v, dout, slope, chunk=64)
+    o, S = prefill_varlen(q, k, v, slope, cu_seqlens, chunk=128)   # q: [H, T, d] packed
 
 The operation (Ling & Ring 2.6 Technical Report pages, "Hybrid Linear
 Attention" section): per head, lambda = exp(-slope[h]),
@@ -46,6 +47,9 @@ SIGNATURES = {
     "la_decode_step": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "la_prefill_bwd": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "la_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
+    "la_prefill_varlen": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "la_prefill_bwd_varlen": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "la_workspace_bytes_varlen": (_Z, [_I, _I, _I, _I, _I, _I, _P]),
     "la_status_string": (ctypes.c_char_p, [_I]),
     "la_abi_version": (_I, []),
 }
@@ -219,6 +223,78 @@ def prefill_bwd(q, k, v, dout, slope, chunk=64, dq=None, dk=None, dv=None,
         None if ws is None else ws.data_ptr(), wsb, _stream(stream),
     )
     _check("la_prefill_bwd", code)
+    return dq, dk, dv
+
+
+def _cu_array(cu_seqlens):
+    """cu_seqlens (a list, numpy array or CPU tensor of nseq + 1 ints) as a
+    host int32 ctypes array, the form the library reads."""
+    if isinstance(cu_seqlens, torch.Tensor):
+        if cu_seqlens.is_cuda:
+            raise TypeError("cu_seqlens must be host data (list, numpy array or CPU tensor)")
+        cu_seqlens = cu_seqlens.tolist()
+    vals = [int(x) for x in cu_seqlens]
+    return len(vals) - 1, (ctypes.c_int * len(vals))(*vals)
+
+
+def workspace_bytes_varlen(op: int, dtype: int, H: int, d: int, C: int, cu_seqlens) -> int:
+    nseq, cu = _cu_array(cu_seqlens)
+    n = lib().la_workspace_bytes_varlen(op, dtype, H, d, C, nseq, cu)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("arguments rejected by la_workspace_bytes_varlen")
+    return n
+
+
+def prefill_varlen(q, k, v, slope, cu_seqlens, chunk=64, state_in=None, out=None,
+                   state_out=None, return_state=True, workspace=None, stream=None):
+    """Packed batch: q, k, v [H,T,d]; sequence s is tokens
+    cu_seqlens[s] .. cu_seqlens[s+1]-1 (host ints).  Returns (o, state_out)
+    with state_out [nseq,H,d,d] fp32 (None when return_state is False and no
+    state_out tensor is given)."""
+    H, T, d = q.shape
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("%s must match q in shape and dtype" % name)
+    nseq, cu = _cu_array(cu_seqlens)
+    if out is None:
+        out = torch.empty_like(q)
+    if state_out is None and return_state:
+        state_out = torch.empty((nseq, H, d, d), dtype=torch.float32, device=q.device)
+    nbytes = workspace_bytes_varlen(0, dt, H, d, chunk, cu_seqlens)
+    ws, wsb = _workspace(nbytes, q.device, workspace)
+    code = lib().la_prefill_varlen(
+        dt, H, d, chunk, nseq, cu,
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(slope, "slope", torch.float32),
+        None if state_in is None else _dev(state_in, "state_in", torch.float32),
+        _dev(out, "out", q.dtype),
+        None if state_out is None else _dev(state_out, "state_out", torch.float32),
+        None if ws is None else ws.data_ptr(), wsb, _stream(stream),
+    )
+    _check("la_prefill_varlen", code)
+    return out, state_out
+
+
+def prefill_bwd_varlen(q, k, v, dout, slope, cu_seqlens, chunk=64, dq=None, dk=None, dv=None,
+                       workspace=None, stream=None):
+    """Gradients (dq, dk, dv) [H,T,d] of sum(o * dout) for o = prefill_varlen(...)
+    with zero initial states."""
+    H, T, d = q.shape
+    dt = _dtype_code(q)
+    nseq, cu = _cu_array(cu_seqlens)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    nbytes = workspace_bytes_varlen(1, dt, H, d, chunk, cu_seqlens)
+    ws, wsb = _workspace(nbytes, q.device, workspace)
+    code = lib().la_prefill_bwd_varlen(
+        dt, H, d, chunk, nseq, cu,
+        _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(dout, "dout", q.dtype),
+        _dev(slope, "slope", torch.float32),
+        _dev(dq, "dq", q.dtype), _dev(dk, "dk", q.dtype), _dev(dv, "dv", q.dtype),
+        None if ws is None else ws.data_ptr(), wsb, _stream(stream),
+    )
+    _check("la_prefill_bwd_varlen", code)
     return dq, dk, dv
 
 

@@ -19,9 +19,27 @@ constexpr int kMaxPieceLen = 1024;
 
 struct Plan {
   int nseg = 1, seg_len = 0, piece_len = 0, npiece = 0;
+  int G = 0;             // packed batches: segments per head
+  bool prepass = false;  // some row has more than one segment
   size_t pieces_bytes = 0, seg_bytes = 0;
   size_t ws() const { return pieces_bytes + seg_bytes; }
 };
+
+// The uniform layout's (empty) sequence table.
+const la::SeqTable& uniform_table() {
+  static const la::SeqTable t{};
+  return t;
+}
+
+// Largest piece length (a multiple of C dividing seg_len, at most
+// kMaxPieceLen tokens).
+int piece_len_for(int seg_len, int C) {
+  const int seg_chunks = seg_len / C;
+  int pc = 1;
+  for (int x = 1; x <= seg_chunks; ++x)
+    if (seg_chunks % x == 0 && (long long)x * C <= kMaxPieceLen) pc = x;
+  return pc * C;
+}
 
 bool d_ok(la_dtype_t dt, int d) {
   if (dt == LA_BF16) return d == 64 || d == 128;
@@ -45,14 +63,53 @@ Plan make_plan(la_dtype_t dt, int B, int H, int N, int d, int C) {
   p.nseg = nseg;
   p.seg_len = seg_chunks * C;
   if (nseg > 1) {
-    int pc = 1;
-    for (int x = 1; x <= seg_chunks; ++x)
-      if (seg_chunks % x == 0 && (long long)x * C <= kMaxPieceLen) pc = x;
-    p.piece_len = pc * C;
-    p.npiece = (nseg - 1) * (seg_chunks / pc);
+    p.prepass = true;
+    p.piece_len = piece_len_for(p.seg_len, C);
+    p.npiece = (nseg - 1) * (p.seg_len / p.piece_len);
     const size_t dd = (size_t)d * d * sizeof(float);
     p.pieces_bytes = (size_t)heads * p.npiece * dd;
     p.seg_bytes = (size_t)heads * nseg * dd;
+  }
+  return p;
+}
+
+// Packed batch (cu already validated): segments of seg_len tokens, chosen so
+// that the H * sum_s ceil(n_s / seg_len) workgroups fill the GPU; every
+// sequence has at least one segment.  Fills t.
+Plan make_plan_packed(la_dtype_t dt, int H, int d, int C, int nseq, const int* cu,
+                      la::SeqTable* t) {
+  Plan p;
+  t->nseq = nseq;
+  t->T = cu[nseq];
+  for (int s = 0; s <= nseq; ++s) t->cu[s] = cu[s];
+  const long long T = cu[nseq];
+  long long L = C;
+  if (dt == LA_BF16) {
+    const long long per_wg = ((long long)H * T + kTargetWorkgroups - 1) / kTargetWorkgroups;
+    L = ((per_wg + C - 1) / C) * C;
+    if (L < C) L = C;
+  } else {
+    L = T > 0 ? T : 1;  // the fp32 path runs every sequence whole
+  }
+  int g = 0;
+  bool multi = false;
+  for (int s = 0; s < nseq; ++s) {
+    t->g0[s] = g;
+    const long long n = cu[s + 1] - cu[s];
+    const int ns = n > L ? (int)((n + L - 1) / L) : 1;
+    multi = multi || ns > 1;
+    g += ns;
+  }
+  t->g0[nseq] = g;
+  p.G = g;
+  p.seg_len = (int)L;
+  p.nseg = 0;  // per sequence: g0[s+1] - g0[s]
+  if (multi) {
+    p.prepass = true;
+    p.piece_len = piece_len_for(p.seg_len, C);
+    const size_t dd = (size_t)d * d * sizeof(float);
+    p.pieces_bytes = (size_t)H * g * (p.seg_len / p.piece_len) * dd;
+    p.seg_bytes = (size_t)H * g * dd;
   }
   return p;
 }
@@ -78,6 +135,7 @@ la_status_t check_seq(la_dtype_t dt, int B, int H, int N, int d, int C) {
 la::FwdPass make_fwd(const Plan& pl, int B, int H, int N, int d, int C, const void* q,
                      const void* k, const void* v, const float* slope, const float* state_in,
                      void* o, float* state_out, bool reverse, void* workspace) {
+  // (packed batches: B = 1, N = T, and the sequence table travels beside)
   la::FwdPass fp{};
   fp.q = q;
   fp.k = k;
@@ -94,15 +152,16 @@ la::FwdPass make_fwd(const Plan& pl, int B, int H, int N, int d, int C, const vo
   fp.reverse = reverse;
   fp.seg_len = pl.seg_len;
   fp.nseg = pl.nseg;
-  if (pl.nseg > 1) fp.seg_states = (const float*)((const char*)workspace + pl.pieces_bytes);
+  fp.G = pl.G;
+  if (pl.prepass) fp.seg_states = (const float*)((const char*)workspace + pl.pieces_bytes);
   return fp;
 }
 
 // Segment start states (piece kernel + scan); nothing when there is one segment.
-la_status_t run_prepass(const Plan& pl, int B, int H, int N, int d, int C, const void* k,
-                        const void* v, const float* slope, const float* state_in, bool reverse,
-                        void* workspace, hipStream_t s) {
-  if (pl.nseg <= 1) return LA_OK;
+la_status_t run_prepass(const Plan& pl, const la::SeqTable& t, int B, int H, int N, int d, int C,
+                        const void* k, const void* v, const float* slope, const float* state_in,
+                        bool reverse, void* workspace, hipStream_t s) {
+  if (!pl.prepass) return LA_OK;
   float* pieces = (float*)workspace;
   float* seg_states = (float*)((char*)workspace + pl.pieces_bytes);
   la::PiecePass pp{};
@@ -120,7 +179,8 @@ la_status_t run_prepass(const Plan& pl, int B, int H, int N, int d, int C, const
   pp.npiece = pl.npiece;
   pp.seg_len = pl.seg_len;
   pp.nseg = pl.nseg;
-  la_status_t st = hip_status(la::launch_pieces_bf16(pp, s));
+  pp.G = pl.G;
+  la_status_t st = hip_status(la::launch_pieces_bf16(pp, t, s));
   if (st != LA_OK) return st;
   la::ScanPass sp{};
   sp.pieces = pieces;
@@ -135,24 +195,27 @@ la_status_t run_prepass(const Plan& pl, int B, int H, int N, int d, int C, const
   sp.npiece = pl.npiece;
   sp.seg_len = pl.seg_len;
   sp.nseg = pl.nseg;
-  return hip_status(la::launch_scan(sp, s));
+  sp.G = pl.G;
+  return hip_status(la::launch_scan(sp, t, s));
 }
 
-la_status_t run_main(la_dtype_t dt, const la::FwdPass& fp, hipStream_t s) {
-  if (dt == LA_F32) return hip_status(la::launch_fwd_f32(fp, s));
-  return hip_status(la::launch_fwd_bf16(fp, s));
+la_status_t run_main(la_dtype_t dt, const la::FwdPass& fp, const la::SeqTable& t,
+                     hipStream_t s) {
+  if (dt == LA_F32) return hip_status(la::launch_fwd_f32(fp, t, s));
+  return hip_status(la::launch_fwd_bf16(fp, t, s));
 }
 
 // One causal (or, with reverse, anti-causal) pass with its segment pre-pass.
-la_status_t run_pass(la_dtype_t dt, const Plan& pl, int B, int H, int N, int d, int C,
-                     const void* q, const void* k, const void* v, const float* slope,
-                     const float* state_in, void* o, float* state_out, bool reverse,
-                     void* workspace, hipStream_t s) {
-  la_status_t st = run_prepass(pl, B, H, N, d, C, k, v, slope, state_in, reverse, workspace, s);
+la_status_t run_pass(la_dtype_t dt, const Plan& pl, const la::SeqTable& t, int B, int H, int N,
+                     int d, int C, const void* q, const void* k, const void* v,
+                     const float* slope, const float* state_in, void* o, float* state_out,
+                     bool reverse, void* workspace, hipStream_t s) {
+  la_status_t st =
+      run_prepass(pl, t, B, H, N, d, C, k, v, slope, state_in, reverse, workspace, s);
   if (st != LA_OK) return st;
   return run_main(dt, make_fwd(pl, B, H, N, d, C, q, k, v, slope, state_in, o, state_out,
                                reverse, workspace),
-                  s);
+                  t, s);
 }
 
 // Checks of la_prefill / la_prefill_main (q and o may be null for the prepass).
@@ -183,6 +246,28 @@ la_status_t check_prefill(la_dtype_t dt, int B, int H, int N, int d, int C, cons
   return LA_OK;
 }
 
+// Checks shared by the packed-batch calls; fills t and the plan.
+la_status_t check_packed(la_dtype_t dt, int H, int d, int C, int nseq, const int* cu,
+                         la::SeqTable* t, Plan* plan) {
+  if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_BAD_DTYPE;
+  if (H < 1 || nseq < 1 || !d_ok(dt, d) || !c_ok(C)) return LA_ERR_BAD_SHAPE;
+  if (dt == LA_BF16 && C < 32) return LA_ERR_UNSUPPORTED;
+  if (nseq > la::kMaxSeqs) return LA_ERR_UNSUPPORTED;
+  if (!cu) return LA_ERR_NULL_POINTER;
+  if (cu[0] != 0) return LA_ERR_BAD_SHAPE;
+  for (int s = 0; s < nseq; ++s)
+    if (cu[s + 1] < cu[s]) return LA_ERR_BAD_SHAPE;
+  if ((long long)H * cu[nseq] > (1LL << 31) / 2) return LA_ERR_UNSUPPORTED;
+  *plan = make_plan_packed(dt, H, d, C, nseq, cu, t);
+  return LA_OK;
+}
+
+la_status_t check_workspace(const Plan& pl, const void* workspace, size_t workspace_bytes) {
+  if (pl.ws() > 0 && (!workspace || workspace_bytes < pl.ws())) return LA_ERR_WORKSPACE;
+  if (pl.ws() > 0 && !aligned16(workspace)) return LA_ERR_ALIGNMENT;
+  return LA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -196,8 +281,8 @@ la_status_t la_prefill(la_dtype_t dt, int B, int H, int N, int d, int C, const v
     const la_status_t st = check_prefill(dt, B, H, N, d, C, q, k, v, slope, state_in, o,
                                          state_out, workspace, workspace_bytes, true, &pl);
     if (st != LA_OK) return st;
-    return run_pass(dt, pl, B, H, N, d, C, q, k, v, slope, state_in, o, state_out, false,
-                    workspace, (hipStream_t)stream);
+    return run_pass(dt, pl, uniform_table(), B, H, N, d, C, q, k, v, slope, state_in, o,
+                    state_out, false, workspace, (hipStream_t)stream);
   } catch (...) {
     return LA_ERR_HIP;
   }
@@ -211,8 +296,8 @@ la_status_t la_prefill_prepass(la_dtype_t dt, int B, int H, int N, int d, int C,
     const la_status_t st = check_prefill(dt, B, H, N, d, C, nullptr, k, v, slope, state_in,
                                          nullptr, nullptr, workspace, workspace_bytes, false, &pl);
     if (st != LA_OK) return st;
-    return run_prepass(pl, B, H, N, d, C, k, v, slope, state_in, false, workspace,
-                       (hipStream_t)stream);
+    return run_prepass(pl, uniform_table(), B, H, N, d, C, k, v, slope, state_in, false,
+                       workspace, (hipStream_t)stream);
   } catch (...) {
     return LA_ERR_HIP;
   }
@@ -230,7 +315,7 @@ la_status_t la_prefill_main(la_dtype_t dt, int B, int H, int N, int d, int C, co
     return run_main(dt,
                     make_fwd(pl, B, H, N, d, C, q, k, v, slope, state_in, o, state_out, false,
                              workspace),
-                    (hipStream_t)stream);
+                    uniform_table(), (hipStream_t)stream);
   } catch (...) {
     return LA_ERR_HIP;
   }
@@ -288,19 +373,103 @@ la_status_t la_prefill_bwd(la_dtype_t dt, int B, int H, int N, int d, int C, con
     if (pl.ws() > 0 && !aligned16(workspace)) return LA_ERR_ALIGNMENT;
     const hipStream_t s = (hipStream_t)stream;
     // dq_t = S_t dout_t: the causal pass with (q, k, v) -> (dout, v, k)
-    st = run_pass(dt, pl, B, H, N, d, C, dout, v, k, slope, nullptr, dq, nullptr, false,
-                  workspace, s);
+    st = run_pass(dt, pl, uniform_table(), B, H, N, d, C, dout, v, k, slope, nullptr, dq,
+                  nullptr, false, workspace, s);
     if (st != LA_OK) return st;
     // dk_s = sum_{t>=s} lambda^(t-s) (v_s . dout_t) q_t: anti-causal, (v, dout, q)
-    st = run_pass(dt, pl, B, H, N, d, C, v, dout, q, slope, nullptr, dk, nullptr, true,
-                  workspace, s);
+    st = run_pass(dt, pl, uniform_table(), B, H, N, d, C, v, dout, q, slope, nullptr, dk,
+                  nullptr, true, workspace, s);
     if (st != LA_OK) return st;
     // dv_s = sum_{t>=s} lambda^(t-s) (k_s . q_t) dout_t: anti-causal, (k, q, dout)
-    return run_pass(dt, pl, B, H, N, d, C, k, q, dout, slope, nullptr, dv, nullptr, true,
+    return run_pass(dt, pl, uniform_table(), B, H, N, d, C, k, q, dout, slope, nullptr, dv,
+                    nullptr, true, workspace, s);
+  } catch (...) {
+    return LA_ERR_HIP;
+  }
+}
+
+la_status_t la_prefill_varlen(la_dtype_t dt, int H, int d, int C, int nseq,
+                              const int* cu_seqlens, const void* q, const void* k,
+                              const void* v, const float* slope, const float* state_in, void* o,
+                              float* state_out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  try {
+    la::SeqTable t;
+    Plan pl;
+    la_status_t st = check_packed(dt, H, d, C, nseq, cu_seqlens, &t, &pl);
+    if (st != LA_OK) return st;
+    if (!q || !k || !v || !o || !slope) return LA_ERR_NULL_POINTER;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state_in) ||
+        !aligned16(state_out) || ((uintptr_t)slope & 3u))
+      return LA_ERR_ALIGNMENT;
+    const size_t esz = dt == LA_BF16 ? 2 : 4;
+    const size_t tb = (size_t)H * t.T * d * esz;
+    const size_t sb = (size_t)nseq * H * d * d * sizeof(float);
+    if (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb))
+      return LA_ERR_ALIAS;
+    if (state_in && state_out && state_in != state_out && overlap(state_in, sb, state_out, sb))
+      return LA_ERR_ALIAS;
+    if (state_out && (overlap(state_out, sb, q, tb) || overlap(state_out, sb, k, tb) ||
+                      overlap(state_out, sb, v, tb) || overlap(state_out, sb, o, tb)))
+      return LA_ERR_ALIAS;
+    st = check_workspace(pl, workspace, workspace_bytes);
+    if (st != LA_OK) return st;
+    return run_pass(dt, pl, t, 1, H, t.T, d, C, q, k, v, slope, state_in, o, state_out, false,
+                    workspace, (hipStream_t)stream);
+  } catch (...) {
+    return LA_ERR_HIP;
+  }
+}
+
+la_status_t la_prefill_bwd_varlen(la_dtype_t dt, int H, int d, int C, int nseq,
+                                  const int* cu_seqlens, const void* q, const void* k,
+                                  const void* v, const void* dout, const float* slope, void* dq,
+                                  void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  try {
+    la::SeqTable t;
+    Plan pl;
+    la_status_t st = check_packed(dt, H, d, C, nseq, cu_seqlens, &t, &pl);
+    if (st != LA_OK) return st;
+    if (!q || !k || !v || !dout || !slope || !dq || !dk || !dv) return LA_ERR_NULL_POINTER;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)slope & 3u))
+      return LA_ERR_ALIGNMENT;
+    const size_t esz = dt == LA_BF16 ? 2 : 4;
+    const size_t tb = (size_t)H * t.T * d * esz;
+    const void* ins[4] = {q, k, v, dout};
+    void* outs[3] = {dq, dk, dv};
+    for (int a = 0; a < 3; ++a) {
+      for (int b = 0; b < 4; ++b)
+        if (overlap(outs[a], tb, ins[b], tb)) return LA_ERR_ALIAS;
+      for (int b = a + 1; b < 3; ++b)
+        if (overlap(outs[a], tb, outs[b], tb)) return LA_ERR_ALIAS;
+    }
+    st = check_workspace(pl, workspace, workspace_bytes);
+    if (st != LA_OK) return st;
+    const hipStream_t s = (hipStream_t)stream;
+    const int T = t.T;
+    // the three passes of la_prefill_bwd, each sequence reversed in place
+    st = run_pass(dt, pl, t, 1, H, T, d, C, dout, v, k, slope, nullptr, dq, nullptr, false,
+                  workspace, s);
+    if (st != LA_OK) return st;
+    st = run_pass(dt, pl, t, 1, H, T, d, C, v, dout, q, slope, nullptr, dk, nullptr, true,
+                  workspace, s);
+    if (st != LA_OK) return st;
+    return run_pass(dt, pl, t, 1, H, T, d, C, k, q, dout, slope, nullptr, dv, nullptr, true,
                     workspace, s);
   } catch (...) {
     return LA_ERR_HIP;
   }
+}
+
+size_t la_workspace_bytes_varlen(int op, la_dtype_t dt, int H, int d, int C, int nseq,
+                                 const int* cu_seqlens) {
+  if (op != 0 && op != 1) return (size_t)-1;
+  la::SeqTable t;
+  Plan pl;
+  if (check_packed(dt, H, d, C, nseq, cu_seqlens, &t, &pl) != LA_OK) return (size_t)-1;
+  return pl.ws();
 }
 
 size_t la_workspace_bytes(int op, la_dtype_t dt, int B, int H, int N, int d, int C) {

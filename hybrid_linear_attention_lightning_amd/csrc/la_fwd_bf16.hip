@@ -89,7 +89,8 @@ __host__ __device__ constexpr int swz_of(int r) {
 }
 
 template <int C, int D, bool STATE_ONLY>
-__global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PiecePass pp) {
+__global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PiecePass pp,
+                                                                const SeqTable st) {
   using G = Cfg<C, D, STATE_ONLY>;
   constexpr int kThreads = G::THREADS;
   constexpr int CT = G::CT;
@@ -99,7 +100,12 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
   const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
 
   // ---- work item -------------------------------------------------------
-  int bh, tau0, tau_end, N, H;
+  // One (sequence, head) row and a token range [tau0, tau_end) of it; token
+  // positions count from the row's first token (or from its last one when
+  // the pass runs backwards in time).
+  const bool packed = st.nseq > 0;
+  Row row;
+  int tau0, tau_end;
   bool reverse;
   const float* slope;
   const uint16_t *qg = nullptr, *kg, *vg;
@@ -113,49 +119,63 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
     // all XCDs (consecutive ids go to different XCDs), and the workgroups
     // that exit at once come last.
     const int ppseg = pp.seg_len / pp.piece_len;
-    const int groups = pp.B * pp.H * (pp.nseg - 1);
+    const int per_row = packed ? pp.G : pp.nseg - 1;  // segment groups per row / head
+    const int groups = (packed ? pp.H : pp.B * pp.H) * per_row;
     const int rank = blockIdx.x / groups;  // 0 = last piece of its segment
     const int g = blockIdx.x - rank * groups;
-    const int sidx = g % (pp.nseg - 1);
-    const int piece = sidx * ppseg + (ppseg - 1 - rank);
-    bh = g / (pp.nseg - 1);
-    H = pp.H;
-    N = pp.N;
+    int seg;
+    if (packed) {
+      const int h = g / per_row, gs = g - h * per_row;
+      const int sq = seq_of_segment(st, gs);
+      row = packed_row(st, sq, h, pp.H, pp.G, ppseg);
+      seg = gs - st.g0[sq];
+    } else {
+      row = uniform_row(g / per_row, pp.H, pp.N, pp.nseg, pp.npiece);
+      seg = g % per_row;
+    }
+    const int piece = seg * ppseg + (ppseg - 1 - rank);
     reverse = pp.reverse;
     slope = pp.slope;
     tau0 = piece * pp.piece_len;
-    tau_end = min(N, tau0 + pp.piece_len);
+    tau_end = min(row.len, tau0 + pp.piece_len);
     // needed only if the nearest segment start at or after the piece end is
     // a real segment start and the decay over the gap is not negligible
     const int r_star = (tau_end + pp.seg_len - 1) / pp.seg_len;
-    if (r_star > pp.nseg - 1) return;
+    if (tau0 >= tau_end || r_star > row.nseg - 1) return;
     const float gap = (float)(r_star * pp.seg_len - tau_end);
-    if (slope[bh % H] * kLog2e * gap >= kSkipLog2) return;
-    const size_t head_off = (size_t)bh * (size_t)N * D;
+    if (slope[row.h] * kLog2e * gap >= kSkipLog2) return;
+    const size_t head_off = row.tok * D;
     kg = (const uint16_t*)pp.k + head_off;
     vg = (const uint16_t*)pp.v + head_off;
-    s_final = pp.pieces + ((size_t)bh * pp.npiece + piece) * D * D;
+    s_final = pp.pieces + ((size_t)row.piecebase + piece) * D * D;
   } else {
-    const int seg = blockIdx.x % p.nseg;
-    bh = blockIdx.x / p.nseg;
-    H = p.H;
-    N = p.N;
+    int seg;
+    if (packed) {
+      const int h = blockIdx.x / p.G, gs = blockIdx.x - h * p.G;
+      const int sq = seq_of_segment(st, gs);
+      row = packed_row(st, sq, h, p.H, p.G, 0);
+      seg = gs - st.g0[sq];
+    } else {
+      row = uniform_row(blockIdx.x / p.nseg, p.H, p.N, p.nseg, 0);
+      seg = blockIdx.x % p.nseg;
+    }
     reverse = p.reverse;
     slope = p.slope;
     tau0 = seg * p.seg_len;
-    tau_end = min(N, tau0 + p.seg_len);
-    const size_t head_off = (size_t)bh * (size_t)N * D;
+    tau_end = min(row.len, tau0 + p.seg_len);
+    const size_t head_off = row.tok * D;
     qg = (const uint16_t*)p.q + head_off;
     kg = (const uint16_t*)p.k + head_off;
     vg = (const uint16_t*)p.v + head_off;
     og = (uint16_t*)p.o + head_off;
     if (seg == 0)
-      s_init = p.state_in ? p.state_in + (size_t)bh * D * D : nullptr;
+      s_init = p.state_in ? p.state_in + (size_t)row.st * D * D : nullptr;
     else
-      s_init = p.seg_states + ((size_t)bh * p.nseg + seg) * D * D;
-    if (seg == p.nseg - 1 && p.state_out) s_final = p.state_out + (size_t)bh * D * D;
+      s_init = p.seg_states + ((size_t)row.segbase + seg) * D * D;
+    if (seg == row.nseg - 1 && p.state_out) s_final = p.state_out + (size_t)row.st * D * D;
   }
-  const float sl2 = slope[bh % H] * kLog2e;  // lambda^e = exp2(-sl2 * e)
+  const int N = row.len;  // reversed positions count back from the row's last token
+  const float sl2 = slope[row.h] * kLog2e;  // lambda^e = exp2(-sl2 * e)
   const int col0 = 32 * wave;                // this wave's first value column
 
   // ---- fp32 state: S[t][ct][r] = S[feature feat(t, r)][value col0 + 16ct + li]
@@ -617,47 +637,50 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
 }
 
 template <int C, int D>
-hipError_t launch_fwd_cd(const FwdPass& p, hipStream_t s) {
+hipError_t launch_fwd_cd(const FwdPass& p, const SeqTable& t, hipStream_t s) {
   PiecePass none{};
-  const unsigned grid = (unsigned)(p.B * p.H * p.nseg);
-  hipLaunchKernelGGL((fwd_bf16_kernel<C, D, false>), dim3(grid), dim3(D / 32 * 64), 0, s, p, none);
+  const unsigned grid = (unsigned)(t.nseq > 0 ? p.H * p.G : p.B * p.H * p.nseg);
+  hipLaunchKernelGGL((fwd_bf16_kernel<C, D, false>), dim3(grid), dim3(D / 32 * 64), 0, s, p, none,
+                     t);
   return hipGetLastError();
 }
 
 template <int C, int D>
-hipError_t launch_pieces_cd(const PiecePass& pp, hipStream_t s) {
+hipError_t launch_pieces_cd(const PiecePass& pp, const SeqTable& t, hipStream_t s) {
   FwdPass none{};
-  const unsigned grid = (unsigned)(pp.B * pp.H * pp.npiece);
-  hipLaunchKernelGGL((fwd_bf16_kernel<C, D, true>), dim3(grid), dim3(D / 32 * 64), 0, s, none, pp);
+  const unsigned grid = (unsigned)(t.nseq > 0 ? pp.H * pp.G * (pp.seg_len / pp.piece_len)
+                                              : pp.B * pp.H * pp.npiece);
+  hipLaunchKernelGGL((fwd_bf16_kernel<C, D, true>), dim3(grid), dim3(D / 32 * 64), 0, s, none, pp,
+                     t);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdPass& p, hipStream_t s) {
+hipError_t launch_fwd_bf16(const FwdPass& p, const SeqTable& t, hipStream_t s) {
   if (p.D == 128) {
-    if (p.C == 128) return launch_fwd_cd<128, 128>(p, s);
-    if (p.C == 64) return launch_fwd_cd<64, 128>(p, s);
-    if (p.C == 32) return launch_fwd_cd<32, 128>(p, s);
+    if (p.C == 128) return launch_fwd_cd<128, 128>(p, t, s);
+    if (p.C == 64) return launch_fwd_cd<64, 128>(p, t, s);
+    if (p.C == 32) return launch_fwd_cd<32, 128>(p, t, s);
   } else if (p.D == 64) {
-    if (p.C == 128) return launch_fwd_cd<128, 64>(p, s);
-    if (p.C == 64) return launch_fwd_cd<64, 64>(p, s);
-    if (p.C == 32) return launch_fwd_cd<32, 64>(p, s);
+    if (p.C == 128) return launch_fwd_cd<128, 64>(p, t, s);
+    if (p.C == 64) return launch_fwd_cd<64, 64>(p, t, s);
+    if (p.C == 32) return launch_fwd_cd<32, 64>(p, t, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_pieces_bf16(const PiecePass& p, hipStream_t s) {
+hipError_t launch_pieces_bf16(const PiecePass& p, const SeqTable& t, hipStream_t s) {
   // A piece state does not depend on the chunk length it is accumulated in,
   // and piece lengths are multiples of C.  Chunks of at most 64 tokens keep
   // the double-buffered K and V tiles at 64 KB (d = 128), so two workgroups
   // share a CU and hide each other's load latency.
   if (p.D == 128) {
-    if (p.C >= 64) return launch_pieces_cd<64, 128>(p, s);
-    if (p.C == 32) return launch_pieces_cd<32, 128>(p, s);
+    if (p.C >= 64) return launch_pieces_cd<64, 128>(p, t, s);
+    if (p.C == 32) return launch_pieces_cd<32, 128>(p, t, s);
   } else if (p.D == 64) {
-    if (p.C >= 64) return launch_pieces_cd<64, 64>(p, s);
-    if (p.C == 32) return launch_pieces_cd<32, 64>(p, s);
+    if (p.C >= 64) return launch_pieces_cd<64, 64>(p, t, s);
+    if (p.C == 32) return launch_pieces_cd<32, 64>(p, t, s);
   }
   return hipErrorInvalidValue;
 }

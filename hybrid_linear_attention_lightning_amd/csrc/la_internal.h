@@ -7,6 +7,22 @@
 
 namespace la {
 
+// Packed (variable-length) batches.  nseq == 0: the uniform layout, token
+// tensors [B][H][N][D] and states [B][H][D][D].  nseq > 0: token tensors
+// [H][T][D] holding nseq sequences back to back, sequence s on tokens
+// cu[s] .. cu[s+1]-1 of every head, states [nseq][H][D][D]; each sequence is
+// its own recurrence from its own initial state.  Segments (see FwdPass) are
+// numbered per head across the sequences: sequence s owns segments
+// g0[s] .. g0[s+1]-1, at least one even when it is empty.  The table travels
+// to the kernels by value, as a kernel argument.
+constexpr int kMaxSeqs = 256;
+struct SeqTable {
+  int nseq;
+  int T;
+  int cu[kMaxSeqs + 1];
+  int g0[kMaxSeqs + 1];
+};
+
 // One causal chunked pass o_t = sum_{s<=t} lambda^(t-s) (q_t . k_s) v_s
 // (+ lambda^(t+1) q_t^T S_in) over [B][H][N][D] token tensors.  With
 // reverse = true the pass runs over the time-reversed sequence (token
@@ -24,10 +40,12 @@ struct FwdPass {
   bool reverse;
   // Segment parallelism: the sequence is cut into nseg segments of seg_len
   // tokens (a multiple of C); segment r > 0 starts from seg_states[b][h][r]
-  // (entry r = 0 is unused and state_in is used instead).
+  // (entry r = 0 is unused and state_in is used instead).  Packed batches:
+  // G segments per head, seg_states[h][g].
   int seg_len;
   int nseg;
-  const float* seg_states;  // [B][H][nseg][D][D] or nullptr when nseg == 1
+  int G;
+  const float* seg_states;  // [B][H][nseg][D][D] / [H][G][D][D], or nullptr
 };
 
 // Per-piece local states for the segment pre-pass:
@@ -37,28 +55,68 @@ struct PiecePass {
   const void* k;
   const void* v;
   const float* slope;
-  float* pieces;  // [B][H][npiece][D][D]
+  float* pieces;  // [B][H][npiece][D][D]; packed: [H][G][seg_len/piece_len][D][D]
   int B, H, N, D, C;
   bool reverse;
   int piece_len, npiece;
   int seg_len, nseg;  // a piece is computed only if some segment start needs it
+  int G;              // packed batches: segments per head
 };
 
 // Segment start states from the piece states (and state_in).
 struct ScanPass {
-  const float* pieces;     // [B][H][npiece][D][D]
-  const float* state_in;   // [B][H][D][D] or nullptr
-  float* seg_states;       // [B][H][nseg][D][D]
+  const float* pieces;     // as PiecePass::pieces
+  const float* state_in;   // [B][H][D][D] / [nseq][H][D][D] or nullptr
+  float* seg_states;       // as FwdPass::seg_states
   const float* slope;
   int B, H, N, D;
   int piece_len, npiece;
   int seg_len, nseg;
+  int G;
 };
 
-hipError_t launch_fwd_bf16(const FwdPass& p, hipStream_t s);
-hipError_t launch_fwd_f32(const FwdPass& p, hipStream_t s);
-hipError_t launch_pieces_bf16(const PiecePass& p, hipStream_t s);
-hipError_t launch_scan(const ScanPass& p, hipStream_t s);
+// One (sequence, head) recurrence of a pass, and where its data lives.
+struct Row {
+  size_t tok;     // its first token row in the token tensors
+  int len;        // tokens
+  int h;          // head (slope index)
+  int st;         // its d x d state in state_in / state_out
+  int segbase;    // its first entry in seg_states
+  int piecebase;  // its first entry in pieces
+  int nseg;       // segments
+};
+
+// Row b*H + h of the uniform layout.
+__host__ __device__ inline Row uniform_row(int bh, int H, int N, int nseg, int npiece) {
+  return Row{(size_t)bh * (size_t)N, N, bh % H, bh, bh * nseg, bh * npiece, nseg};
+}
+
+// Row (s, h) of a packed batch; ppseg = pieces per segment.
+__host__ __device__ inline Row packed_row(const SeqTable& t, int s, int h, int H, int G,
+                                          int ppseg) {
+  const int g = t.g0[s];
+  return Row{(size_t)h * (size_t)t.T + (size_t)t.cu[s], t.cu[s + 1] - t.cu[s], h, s * H + h,
+             h * G + g, (h * G + g) * ppseg, t.g0[s + 1] - g};
+}
+
+// The sequence that owns segment g (0 <= g < g0[nseq]): the largest s with
+// g0[s] <= g; g0 is strictly increasing.
+__host__ __device__ inline int seq_of_segment(const SeqTable& t, int g) {
+  int lo = 0, hi = t.nseq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (t.g0[mid] <= g)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+hipError_t launch_fwd_bf16(const FwdPass& p, const SeqTable& t, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdPass& p, const SeqTable& t, hipStream_t s);
+hipError_t launch_pieces_bf16(const PiecePass& p, const SeqTable& t, hipStream_t s);
+hipError_t launch_scan(const ScanPass& p, const SeqTable& t, hipStream_t s);
 hipError_t launch_decode(bool bf16, int B, int H, int D, const void* q, const void* k,
                          const void* v, const float* slope, float* state, void* o,
                          hipStream_t s);

@@ -25,29 +25,31 @@
 namespace la {
 namespace {
 
-__global__ __launch_bounds__(256) void scan_kernel(ScanPass p) {
-  // grid: (B*H) x (D*D/4/256 blocks); each thread owns one float4 of the state
+__global__ __launch_bounds__(256) void scan_kernel(ScanPass p, const SeqTable st) {
+  // grid: rows x (D*D/4/256 blocks); each thread owns one float4 of the state
   const int D = p.D;
   const int per_head = D * D / 4;
-  const int bh = blockIdx.x / ((per_head + 255) / 256);
+  const int r_idx = blockIdx.x / ((per_head + 255) / 256);
   const int e4 = (blockIdx.x % ((per_head + 255) / 256)) * 256 + threadIdx.x;
   if (e4 >= per_head) return;
-  const int h = bh % p.H;
-  const float sl2 = p.slope[h] * kLog2e;
+  const int ppseg = p.seg_len / p.piece_len;
+  const Row row = st.nseq > 0 ? packed_row(st, r_idx / p.H, r_idx % p.H, p.H, p.G, ppseg)
+                              : uniform_row(r_idx, p.H, p.N, p.nseg, p.npiece);
+  if (row.nseg < 2) return;
+  const float sl2 = p.slope[row.h] * kLog2e;
   const size_t dd = (size_t)D * D;
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-  if (p.state_in) s = reinterpret_cast<const f32x4_t*>(p.state_in + bh * dd)[e4];
+  if (p.state_in) s = reinterpret_cast<const f32x4_t*>(p.state_in + row.st * dd)[e4];
   const float gL = exp2f(-sl2 * (float)p.seg_len);
   // Every segment but the last is full, so the pieces that segment r-1
   // contributes to the start of segment r are the same ranks for every r:
   // rank k (k pieces between it and the segment end) is at distance k * Lp,
   // and it was computed iff lambda^(k Lp) >= 2^-kSkipLog2 (the test the piece
   // kernel makes, in the same arithmetic).
-  const int ppseg = p.seg_len / p.piece_len;
   int nneed = 0;
   while (nneed < ppseg && !(sl2 * (float)(nneed * p.piece_len) >= kSkipLog2)) ++nneed;
-  const f32x4_t* pc4 = reinterpret_cast<const f32x4_t*>(p.pieces + (size_t)bh * p.npiece * dd);
-  for (int r = 1; r < p.nseg; ++r) {
+  const f32x4_t* pc4 = reinterpret_cast<const f32x4_t*>(p.pieces + (size_t)row.piecebase * dd);
+  for (int r = 1; r < row.nseg; ++r) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) s[c] *= gL;
     const int last = r * ppseg - 1;  // piece of rank 0
@@ -65,29 +67,30 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanPass p) {
         for (int c = 0; c < 4; ++c) s[c] = fmaf(f, v[j][c], s[c]);
       }
     }
-    reinterpret_cast<f32x4_t*>(p.seg_states + ((size_t)bh * p.nseg + r) * dd)[e4] = s;
+    reinterpret_cast<f32x4_t*>(p.seg_states + ((size_t)row.segbase + r) * dd)[e4] = s;
   }
 }
 
 template <int D, int CS>
-__global__ __launch_bounds__(256) void fwd_f32_kernel(FwdPass p) {
+__global__ __launch_bounds__(256) void fwd_f32_kernel(FwdPass p, const SeqTable st) {
   constexpr int DS = D + 1;  // padded row stride
   __shared__ float Sm[D * D];
   __shared__ float Qm[CS * DS], Km[CS * DS], Vm[CS * DS];
   __shared__ float Pm[CS * (CS + 1)];
   __shared__ float bj[CS];
   const int tid = threadIdx.x;
-  const int bh = blockIdx.x;
-  const int h = bh % p.H;
-  const int N = p.N;
-  const float sl2 = p.slope[h] * kLog2e;
-  const size_t head_off = (size_t)bh * N * D;
+  // one (sequence, head) row per workgroup
+  const Row row = st.nseq > 0 ? packed_row(st, blockIdx.x / p.H, blockIdx.x % p.H, p.H, 0, 0)
+                              : uniform_row(blockIdx.x, p.H, p.N, 1, 0);
+  const int N = row.len;
+  const float sl2 = p.slope[row.h] * kLog2e;
+  const size_t head_off = row.tok * D;
   const float* qg = (const float*)p.q + head_off;
   const float* kg = (const float*)p.k + head_off;
   const float* vg = (const float*)p.v + head_off;
   float* og = (float*)p.o + head_off;
   for (int e = tid; e < D * D; e += 256)
-    Sm[e] = p.state_in ? p.state_in[(size_t)bh * D * D + e] : 0.f;
+    Sm[e] = p.state_in ? p.state_in[(size_t)row.st * D * D + e] : 0.f;
   auto tok = [&](int tau) { return p.reverse ? (N - 1 - tau) : tau; };
   for (int t0 = 0; t0 < N; t0 += CS) {
     const int n = min(CS, N - t0);
@@ -132,33 +135,34 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdPass p) {
   }
   __syncthreads();
   if (p.state_out)
-    for (int e = tid; e < D * D; e += 256) p.state_out[(size_t)bh * D * D + e] = Sm[e];
+    for (int e = tid; e < D * D; e += 256) p.state_out[(size_t)row.st * D * D + e] = Sm[e];
 }
 
 template <int D, int CS>
-hipError_t launch_f32(const FwdPass& p, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CS>), dim3((unsigned)(p.B * p.H)), dim3(256), 0, s, p);
+hipError_t launch_f32(const FwdPass& p, const SeqTable& t, hipStream_t s) {
+  const unsigned grid = (unsigned)((t.nseq > 0 ? t.nseq : p.B) * p.H);
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CS>), dim3(grid), dim3(256), 0, s, p, t);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_scan(const ScanPass& p, hipStream_t s) {
+hipError_t launch_scan(const ScanPass& p, const SeqTable& t, hipStream_t s) {
   const int per_head = p.D * p.D / 4;
-  const unsigned grid = (unsigned)(p.B * p.H * ((per_head + 255) / 256));
-  hipLaunchKernelGGL(scan_kernel, dim3(grid), dim3(256), 0, s, p);
+  const unsigned grid = (unsigned)((t.nseq > 0 ? t.nseq : p.B) * p.H * ((per_head + 255) / 256));
+  hipLaunchKernelGGL(scan_kernel, dim3(grid), dim3(256), 0, s, p, t);
   return hipGetLastError();
 }
 
 // Chunks are evaluated in blocks of at most min(C, 64) rows (32 for d = 128);
 // the result does not depend on the blocking beyond rounding.
-hipError_t launch_fwd_f32(const FwdPass& p, hipStream_t s) {
+hipError_t launch_fwd_f32(const FwdPass& p, const SeqTable& t, hipStream_t s) {
   const int cs = p.C;
   switch (p.D) {
-    case 16: return cs >= 64 ? launch_f32<16, 64>(p, s) : cs >= 32 ? launch_f32<16, 32>(p, s) : launch_f32<16, 16>(p, s);
-    case 32: return cs >= 64 ? launch_f32<32, 64>(p, s) : cs >= 32 ? launch_f32<32, 32>(p, s) : launch_f32<32, 16>(p, s);
-    case 64: return cs >= 64 ? launch_f32<64, 64>(p, s) : cs >= 32 ? launch_f32<64, 32>(p, s) : launch_f32<64, 16>(p, s);
-    case 128: return cs >= 32 ? launch_f32<128, 32>(p, s) : launch_f32<128, 16>(p, s);
+    case 16: return cs >= 64 ? launch_f32<16, 64>(p, t, s) : cs >= 32 ? launch_f32<16, 32>(p, t, s) : launch_f32<16, 16>(p, t, s);
+    case 32: return cs >= 64 ? launch_f32<32, 64>(p, t, s) : cs >= 32 ? launch_f32<32, 32>(p, t, s) : launch_f32<32, 16>(p, t, s);
+    case 64: return cs >= 64 ? launch_f32<64, 64>(p, t, s) : cs >= 32 ? launch_f32<64, 32>(p, t, s) : launch_f32<64, 16>(p, t, s);
+    case 128: return cs >= 32 ? launch_f32<128, 32>(p, t, s) : launch_f32<128, 16>(p, t, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 1
+#define LA_ABI_VERSION 2
 
 typedef enum {
   LA_OK = 0,
@@ -167,6 +167,64 @@ la_status_t la_prefill_bwd(la_dtype_t dt, int B, int H, int N, int d, int C,
  * for arguments the corresponding call would reject. */
 size_t la_workspace_bytes(int op, la_dtype_t dt, int B, int H, int N, int d,
                           int C);
+
+/* ------------------------------------------------------------------------ *
+ * la_prefill_varlen -- la_prefill over a packed batch of sequences of
+ * different lengths, each with its own initial and final state.
+ *
+ * The pages train on variable-length (packed) batches and fold the state
+ * correction of several sub-sequences into one kernel ("Context Parallel for
+ * Lightning Attention" section), and serve with prefix caching ("linghe"
+ * section): a sequence continues from the cached state of its prefix.  Here
+ * sequence s is tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 of every head, and
+ * is its own recurrence: no token sees a token of another sequence, and its
+ * state starts from state_in[s] (zero when state_in is NULL).  Running a
+ * sequence in two calls, the second with the first's state_out as state_in,
+ * gives the result of one call over the whole sequence.
+ *
+ *   dt, d, C   as for la_prefill;  H >= 1
+ *   nseq       1 .. 256 (more gives LA_ERR_UNSUPPORTED)
+ *   cu_seqlens HOST array of nseq + 1 ints, read during the call only:
+ *              cu_seqlens[0] = 0, non-decreasing (empty sequences allowed);
+ *              T = cu_seqlens[nseq] is the packed length; H*T above 2^30
+ *              gives LA_ERR_UNSUPPORTED
+ *   q, k, v    [H][T][d] of dt (the B = 1 layout of la_prefill with the
+ *              sequences back to back), 16-byte aligned
+ *   slope      [H] fp32
+ *   state_in   [nseq][H][d][d] fp32, or NULL for zero initial states
+ *   o          [H][T][d] of dt, written; must not overlap q, k or v
+ *   state_out  [nseq][H][d][d] fp32 or NULL; may equal state_in, must not
+ *              partially overlap it; an empty sequence's state passes through
+ *   workspace  at least la_workspace_bytes_varlen(0, ...) bytes
+ * Errors as for la_prefill; a malformed cu_seqlens gives LA_ERR_BAD_SHAPE.
+ * ------------------------------------------------------------------------ */
+la_status_t la_prefill_varlen(la_dtype_t dt, int H, int d, int C, int nseq,
+                              const int *cu_seqlens, const void *q,
+                              const void *k, const void *v, const float *slope,
+                              const float *state_in, void *o, float *state_out,
+                              void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* ------------------------------------------------------------------------ *
+ * la_prefill_bwd_varlen -- la_prefill_bwd over a packed batch (zero initial
+ * states): the gradients of L = sum_t o_t . dout_t for o from
+ * la_prefill_varlen with state_in = NULL.  Arguments as for
+ * la_prefill_varlen and la_prefill_bwd; dout, dq, dk, dv are [H][T][d] of dt,
+ * the outputs must not overlap any input or each other; the workspace is at
+ * least la_workspace_bytes_varlen(1, ...) bytes.
+ * ------------------------------------------------------------------------ */
+la_status_t la_prefill_bwd_varlen(la_dtype_t dt, int H, int d, int C, int nseq,
+                                  const int *cu_seqlens, const void *q,
+                                  const void *k, const void *v,
+                                  const void *dout, const float *slope,
+                                  void *dq, void *dk, void *dv, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/* Device workspace bytes for la_prefill_varlen (op = 0) or
+ * la_prefill_bwd_varlen (op = 1); (size_t)-1 for arguments they would
+ * reject. */
+size_t la_workspace_bytes_varlen(int op, la_dtype_t dt, int H, int d, int C,
+                                 int nseq, const int *cu_seqlens);
 
 /* Static, NUL-terminated description of a status code. */
 const char *la_status_string(la_status_t status);

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = la.lib()
-    assert lib.la_abi_version() == 1
+    assert lib.la_abi_version() == 2
     for code in range(9):
         assert lib.la_status_string(code)
     assert lib.la_status_string(123) == b"unknown status"
@@ -104,3 +104,55 @@ def test_workspace_plan():
     with pytest.raises(ValueError):
         la.workspace_bytes(0, BF16, 1, 32, 131072, 100, 128)
     assert la.lib().la_workspace_bytes(2, BF16, 1, 1, 1, 64, 64) == ctypes.c_size_t(-1).value
+
+
+def test_varlen_validation():
+    f = la.lib().la_prefill_varlen
+
+    def call(dt=BF16, H=2, d=128, C=64, cu=(0, 100, 5000), q=Q, o=O, s_in=None, s_out=None,
+             ws=None, wsb=0, nseq=None):
+        n = (len(cu) - 1 if cu is not None else 1) if nseq is None else nseq
+        arr = (ctypes.c_int * len(cu))(*cu) if cu is not None else None
+        return f(dt, H, d, C, n, arr, q, K, V, SLOPE, s_in, o, s_out, ws, wsb, None)
+
+    assert call(dt=5) == DTYPE
+    assert call(H=0) == SHAPE and call(d=96) == SHAPE and call(C=48) == SHAPE
+    assert call(nseq=0) == SHAPE
+    assert call(dt=BF16, C=16) == UNSUP
+    assert call(cu=None) == NULLP
+    assert call(cu=(1, 100)) == SHAPE  # must start at 0
+    assert call(cu=(0, 100, 50)) == SHAPE  # must not decrease
+    assert call(cu=tuple(range(258))) == UNSUP  # 257 sequences
+    assert call(q=None) == NULLP and call(o=None) == NULLP
+    assert call(q=Q + 8) == ALIGN and call(s_out=S_OUT + 4) == ALIGN
+    assert call(o=K) == ALIAS and call(s_in=S_IN, s_out=S_IN + 16) == ALIAS
+    nws = la.workspace_bytes_varlen(0, BF16, 2, 128, 64, (0, 100, 5000))
+    assert nws > 0  # the long sequence is cut into segments
+    assert call() == WS and call(ws=WSP, wsb=nws - 1) == WS and call(ws=WSP + 8, wsb=nws) == ALIGN
+
+
+def test_varlen_backward_validation():
+    f = la.lib().la_prefill_bwd_varlen
+    cu = (ctypes.c_int * 3)(0, 100, 5000)
+
+    def call(dq=DQ, dk=DK, dv=DV, C=64):
+        return f(BF16, 2, 128, C, 2, cu, Q, K, V, DO, SLOPE, dq, dk, dv, None, 0, None)
+
+    assert call(C=16) == UNSUP and call(dq=None) == NULLP
+    assert call(dk=DQ) == ALIAS and call(dv=DO) == ALIAS
+    assert call() == WS
+
+
+def test_varlen_workspace_plan():
+    # enough (sequence, head) rows to fill the GPU: one segment each, no
+    # workspace; the fp32 path never segments
+    assert la.workspace_bytes_varlen(0, BF16, 32, 128, 128, list(range(0, 8001, 1000))) == 0
+    # few rows: sequences are cut into segments
+    assert la.workspace_bytes_varlen(0, BF16, 32, 128, 128, [0, 1000, 2000, 2048]) > 0
+    assert la.workspace_bytes_varlen(0, F32, 2, 64, 64, [0, 100000]) == 0
+    # one 128K-token sequence of 32 heads: the same cut as the uniform plan
+    assert (la.workspace_bytes_varlen(0, BF16, 32, 128, 128, [0, 131072])
+            == la.workspace_bytes(0, BF16, 1, 32, 131072, 128, 128) + 32 * 16 * 64 * 1024)
+    assert la.workspace_bytes_varlen(1, BF16, 2, 64, 64, [0, 0, 0]) == 0
+    cu = (ctypes.c_int * 2)(0, 10)
+    assert la.lib().la_workspace_bytes_varlen(2, BF16, 1, 64, 64, 1, cu) == ctypes.c_size_t(-1).value
