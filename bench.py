@@ -10,6 +10,9 @@ sequence, inputs resident in HBM.  The same line carries:
   * "decode": the batched decode step (B=64, H=32, d=128), 1000 consecutive
     steps with fresh q/k/v each, microseconds per step and HBM fraction;
   * "train": forward + backward at B=4, H=16, N=32768, d=128, chunk 64;
+  * "varlen": a packed batch of 64 ragged sequences (131072 tokens, H=32,
+    d=128, chunk 128) continuing from per-sequence states, forward and
+    backward;
   * "cpu_baseline": the fp64 CPU oracle on a bounded sample of the headline
     workload (the first tokens of all 32 heads), on the host's cores.
 
@@ -247,6 +250,66 @@ def bench_train(args, torch, la, la_inputs):
     return res
 
 
+def bench_varlen(args, torch, la, la_inputs):
+    """Packed batch: 64 sequences of ragged lengths, 131072 tokens in all,
+    H=32, d=128, C=128, every sequence continuing from its own cached state
+    (state_in) and returning its final state; then the backward of the same
+    batch (zero initial states)."""
+    c = la_inputs.CONFIGS["varlen_128k"]
+    H, d, C, nseq, T, seed = c["H"], c["d"], c["C"], c["nseq"], c["T"], c["seed"]
+    dev = torch.device("cuda:0")
+    cu = la_inputs.packed_cu_seqlens(seed, nseq, T)
+    q, k, v = (x[0] for x in la_inputs.qkv_device(seed, 1, H, T, d, dev, torch.bfloat16))
+    dout = la_inputs.upstream_grad_device(seed, 1, H, T, d, dev, torch.bfloat16)[0]
+    slope = torch.from_numpy(la_inputs.slopes(H)).to(dev)
+    S0 = torch.from_numpy(la_inputs.decode_state(seed, nseq, H, d)).to(dev)
+    S = torch.empty_like(S0)
+    o = torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    nws = max(la.workspace_bytes_varlen(0, la.LA_BF16, H, d, C, cu),
+              la.workspace_bytes_varlen(1, la.LA_BF16, H, d, C, cu))
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    steps = max(2, args.train_steps)
+
+    def step(e=None):
+        if e is not None:
+            e[0].record(stream)
+        la.prefill_varlen(q, k, v, slope, cu, chunk=C, state_in=S0, out=o, state_out=S,
+                          workspace=ws, stream=stream)
+        if e is not None:
+            e[1].record(stream)
+        la.prefill_bwd_varlen(q, k, v, dout, slope, cu, chunk=C, dq=dq, dk=dk, dv=dv,
+                              workspace=ws, stream=stream)
+        if e is not None:
+            e[2].record(stream)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    fb = 4 * H * T * d * 2 + 2 * nseq * H * d * d * 4  # q, k, v, o; state in and out
+    bb = 7 * H * T * d * 2
+    lens = [b - a for a, b in zip(cu, cu[1:])]
+    res = {
+        "H": H, "d": d, "C": C, "nseq": nseq, "T": T,
+        "lengths": {"min": min(lens), "max": max(lens), "mean": T / nseq},
+        "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+        "fwd_tokens_per_s": T / (fwd_ms * 1e-3),
+        "fwd_hbm_frac": fb / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "bwd_hbm_frac": bb / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "note": "fwd bytes: q, k, v read, o written, per-sequence states read and written",
+    }
+    del q, k, v, dout, o, dq, dk, dv, ws, S0, S
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(args, la_inputs):
     """The fp64 oracle on the first tokens of the 128K workload (all 32 heads),
     in pieces of 4096 tokens carried through the state, until about
@@ -294,7 +357,7 @@ def main():
     ap.add_argument("--train-steps", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "train"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "train", "varlen"], default=None,
                     help="run one workload only (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB copy (HBM counter calibration)")
@@ -329,6 +392,10 @@ def main():
         log("train fwd+bwd B=4 H=16 N=32K ...")
         out["train"] = bench_train(args, torch, la, la_inputs)
         log("  fwd %.3f ms, bwd %.3f ms" % (out["train"]["fwd_ms"], out["train"]["bwd_ms"]))
+    if args.only in (None, "varlen"):
+        log("varlen fwd+bwd, 64 packed sequences, T=128K ...")
+        out["varlen"] = bench_varlen(args, torch, la, la_inputs)
+        log("  fwd %.3f ms, bwd %.3f ms" % (out["varlen"]["fwd_ms"], out["varlen"]["bwd_ms"]))
     cpu = None
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         log("cpu baseline (oracle) ...")
@@ -356,6 +423,7 @@ def main():
         "prefill": p,
         "decode": out.get("decode"),
         "train": out.get("train"),
+        "varlen": out.get("varlen"),
     }
     print(json.dumps(line), flush=True)
 

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/lightning_la.h"
 #include "la_internal.h"
 
@@ -75,7 +77,8 @@ Plan make_plan(la_dtype_t dt, int B, int H, int N, int d, int C) {
 
 // Packed batch (cu already validated): segments of seg_len tokens, chosen so
 // that the H * sum_s ceil(n_s / seg_len) workgroups fill the GPU; every
-// sequence has at least one segment.  Fills t.
+// sequence has at least one segment.  Sequences are scheduled longest first
+// (ties in sequence order).  Fills t.
 Plan make_plan_packed(la_dtype_t dt, int H, int d, int C, int nseq, const int* cu,
                       la::SeqTable* t) {
   Plan p;
@@ -91,10 +94,14 @@ Plan make_plan_packed(la_dtype_t dt, int H, int d, int C, int nseq, const int* c
   } else {
     L = T > 0 ? T : 1;  // the fp32 path runs every sequence whole
   }
+  for (int i = 0; i < nseq; ++i) t->ord[i] = i;
+  std::stable_sort(t->ord, t->ord + nseq,
+                   [&](int a, int b) { return cu[a + 1] - cu[a] > cu[b + 1] - cu[b]; });
   int g = 0;
   bool multi = false;
-  for (int s = 0; s < nseq; ++s) {
-    t->g0[s] = g;
+  for (int i = 0; i < nseq; ++i) {
+    const int s = t->ord[i];
+    t->g0[i] = g;
     const long long n = cu[s + 1] - cu[s];
     const int ns = n > L ? (int)((n + L - 1) / L) : 1;
     multi = multi || ns > 1;

@@ -117,7 +117,8 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
     // the pieces every head needs (those just before a segment start) take
     // the lowest workgroup ids, so they are dispatched first and spread over
     // all XCDs (consecutive ids go to different XCDs), and the workgroups
-    // that exit at once come last.
+    // that exit at once come last.  Packed batches: head fastest within a
+    // rank, then segments in schedule order.
     const int ppseg = pp.seg_len / pp.piece_len;
     const int per_row = packed ? pp.G : pp.nseg - 1;  // segment groups per row / head
     const int groups = (packed ? pp.H : pp.B * pp.H) * per_row;
@@ -125,10 +126,10 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
     const int g = blockIdx.x - rank * groups;
     int seg;
     if (packed) {
-      const int h = g / per_row, gs = g - h * per_row;
-      const int sq = seq_of_segment(st, gs);
-      row = packed_row(st, sq, h, pp.H, pp.G, ppseg);
-      seg = gs - st.g0[sq];
+      const int gs = g / pp.H, h = g - gs * pp.H;
+      const int i = seq_of_segment(st, gs);
+      row = packed_row(st, i, h, pp.H, pp.G, ppseg);
+      seg = gs - st.g0[i];
     } else {
       row = uniform_row(g / per_row, pp.H, pp.N, pp.nseg, pp.npiece);
       seg = g % per_row;
@@ -151,10 +152,13 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
   } else {
     int seg;
     if (packed) {
-      const int h = blockIdx.x / p.G, gs = blockIdx.x - h * p.G;
-      const int sq = seq_of_segment(st, gs);
-      row = packed_row(st, sq, h, p.H, p.G, 0);
-      seg = gs - st.g0[sq];
+      // head fastest: consecutive workgroups (which go to different XCDs)
+      // take the heads of one segment, so every XCD gets the same share of
+      // each sequence; segments in schedule order, longest sequence first
+      const int gs = blockIdx.x / p.H, h = blockIdx.x - gs * p.H;
+      const int i = seq_of_segment(st, gs);
+      row = packed_row(st, i, h, p.H, p.G, 0);
+      seg = gs - st.g0[i];
     } else {
       row = uniform_row(blockIdx.x / p.nseg, p.H, p.N, p.nseg, 0);
       seg = blockIdx.x % p.nseg;

@@ -11,16 +11,19 @@ namespace la {
 // tensors [B][H][N][D] and states [B][H][D][D].  nseq > 0: token tensors
 // [H][T][D] holding nseq sequences back to back, sequence s on tokens
 // cu[s] .. cu[s+1]-1 of every head, states [nseq][H][D][D]; each sequence is
-// its own recurrence from its own initial state.  Segments (see FwdPass) are
-// numbered per head across the sequences: sequence s owns segments
-// g0[s] .. g0[s+1]-1, at least one even when it is empty.  The table travels
-// to the kernels by value, as a kernel argument.
+// its own recurrence from its own initial state.
+// Work is scheduled longest sequence first: schedule position i holds
+// sequence ord[i] (lengths non-increasing in i).  Segments (see FwdPass) are
+// numbered per head in schedule order: position i owns segments
+// g0[i] .. g0[i+1]-1, at least one even for an empty sequence.  The table
+// travels to the kernels by value, as a kernel argument (3 KB).
 constexpr int kMaxSeqs = 256;
 struct SeqTable {
   int nseq;
   int T;
   int cu[kMaxSeqs + 1];
   int g0[kMaxSeqs + 1];
+  int ord[kMaxSeqs];
 };
 
 // One causal chunked pass o_t = sum_{s<=t} lambda^(t-s) (q_t . k_s) v_s
@@ -91,16 +94,17 @@ __host__ __device__ inline Row uniform_row(int bh, int H, int N, int nseg, int n
   return Row{(size_t)bh * (size_t)N, N, bh % H, bh, bh * nseg, bh * npiece, nseg};
 }
 
-// Row (s, h) of a packed batch; ppseg = pieces per segment.
-__host__ __device__ inline Row packed_row(const SeqTable& t, int s, int h, int H, int G,
+// Row (sequence at schedule position i, head h) of a packed batch; ppseg =
+// pieces per segment.
+__host__ __device__ inline Row packed_row(const SeqTable& t, int i, int h, int H, int G,
                                           int ppseg) {
-  const int g = t.g0[s];
+  const int s = t.ord[i], g = t.g0[i];
   return Row{(size_t)h * (size_t)t.T + (size_t)t.cu[s], t.cu[s + 1] - t.cu[s], h, s * H + h,
-             h * G + g, (h * G + g) * ppseg, t.g0[s + 1] - g};
+             h * G + g, (h * G + g) * ppseg, t.g0[i + 1] - g};
 }
 
-// The sequence that owns segment g (0 <= g < g0[nseq]): the largest s with
-// g0[s] <= g; g0 is strictly increasing.
+// The schedule position that owns segment g (0 <= g < g0[nseq]): the largest
+// i with g0[i] <= g; g0 is strictly increasing.
 __host__ __device__ inline int seq_of_segment(const SeqTable& t, int g) {
   int lo = 0, hi = t.nseq - 1;
   while (lo < hi) {

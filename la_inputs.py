@@ -12,7 +12,9 @@ synthetic stand-ins documented in the design doc):
   * upstream gradient dO ~ N(0, 1);
   * decode state S0 ~ N(0, 0.1^2) in fp32 (variance 0.01);
   * per-head slope s_h = 2^(-8 (h+1) / H), h = 0..H-1, so the decay is
-    lambda_h = exp(-s_h).
+    lambda_h = exp(-s_h);
+  * packed (varlen) batches: sequence boundaries at nseq - 1 distinct cut
+    points drawn uniformly over the packed tokens.
 
 Each tensor draws from numpy.random.default_rng([seed, tensor_id, step]), so a
 tensor never depends on the sizes of the tensors drawn before it.
@@ -98,11 +100,22 @@ def upstream_grad_device(seed: int, B: int, H: int, N: int, d: int, device, torc
     return torch.randn((B, H, N, d), generator=g, device=device, dtype=torch.float32).to(torch_dtype)
 
 
-# The five workloads (seed = config index, 0-based).
+def packed_cu_seqlens(seed: int, nseq: int, T: int) -> list:
+    """cu_seqlens of a packed batch: nseq - 1 distinct cut points drawn
+    uniformly from 1 .. T-1, so lengths run from a few tokens to several
+    times the mean T / nseq (a ragged mix of short and long sequences)."""
+    rng = np.random.default_rng([seed, 6, 0])
+    cuts = np.sort(rng.choice(np.arange(1, T), size=nseq - 1, replace=False))
+    return [0] + [int(x) for x in cuts] + [int(T)]
+
+
+# The five workloads (seed = config index, 0-based), and a packed-batch
+# workload for the varlen path.
 CONFIGS = {
     "tiny_f32": dict(seed=0, dtype="f32", B=1, H=2, N=256, d=64, C=64),
     "prefill_8k": dict(seed=1, dtype="bf16", B=1, H=32, N=8192, d=128, C=64),
     "prefill_128k": dict(seed=2, dtype="bf16", B=1, H=32, N=131072, d=128, C=128),
     "decode_b64": dict(seed=3, dtype="bf16", B=64, H=32, d=128, steps=1000),
     "train_32k": dict(seed=4, dtype="bf16", B=4, H=16, N=32768, d=128, C=64),
+    "varlen_128k": dict(seed=5, dtype="bf16", nseq=64, H=32, T=131072, d=128, C=128),
 }

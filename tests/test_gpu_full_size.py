@@ -110,3 +110,27 @@ def test_train_32k_sampled_heads(oracle_mod):
         assert_close(_host(dq[b:b + 1, h:h + 1]), rq, "bf16", "dq (b=%d,h=%d)" % (b, h))
         assert_close(_host(dk[b:b + 1, h:h + 1]), rk, "bf16", "dk (b=%d,h=%d)" % (b, h))
         assert_close(_host(dv[b:b + 1, h:h + 1]), rv, "bf16", "dv (b=%d,h=%d)" % (b, h))
+
+
+def test_varlen_128k_sampled_heads(oracle_mod):
+    """The benchmark's packed batch (64 ragged sequences, 131072 tokens,
+    H=32, d=128, C=128, per-sequence initial states): every sequence of
+    sampled heads against the oracle."""
+    c = la_inputs.CONFIGS["varlen_128k"]
+    H, d, C, nseq, T, seed = c["H"], c["d"], c["C"], c["nseq"], c["T"], c["seed"]
+    dev = device()
+    cu = la_inputs.packed_cu_seqlens(seed, nseq, T)
+    tq, tk, tv = (x[0] for x in la_inputs.qkv_device(seed, 1, H, T, d, dev, torch.bfloat16))
+    s = la_inputs.slopes(H)
+    S0 = la_inputs.decode_state(seed, nseq, H, d)
+    o, S = la.prefill_varlen(tq, tk, tv, torch.from_numpy(s).to(dev), cu, chunk=C,
+                             state_in=torch.from_numpy(S0).to(dev))
+    torch.cuda.synchronize()
+    heads = [0, 31]
+    q, k, v = (_host(t[heads]) for t in (tq, tk, tv))
+    ro, rS = oracle_mod.fwd_varlen(q, k, v, s[heads], cu, S0[:, heads])
+    go, gS = _host(o[heads]), _host(S[:, heads])
+    for i, h in enumerate(heads):
+        assert_close(go[i], ro[i], "bf16", "o head %d" % h)
+        assert_close(gS[:, i], rS[:, i], "bf16", "S head %d" % h, stored_bf16=False)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
