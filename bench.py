@@ -9,6 +9,8 @@ sequence, inputs resident in HBM.  The same line carries:
     its HIP-event-timed average duration, against 8 TB/s;
   * "decode": the batched decode step (B=64, H=32, d=128), 1000 consecutive
     steps with fresh q/k/v each, microseconds per step and HBM fraction;
+  * "decode_tokens": 4 new tokens per (b, h) per call on the same state
+    (multi-token generation / draft verification), microseconds per call;
   * "train": forward + backward at B=4, H=16, N=32768, d=128, chunk 64;
   * "varlen": a packed batch of 64 ragged sequences (131072 tokens, H=32,
     d=128, chunk 128) continuing from per-sequence states, forward and
@@ -195,6 +197,49 @@ def bench_decode(args, torch, la, la_inputs):
                      "bytes_per_launch": bytes_},
         "note": "the 134 MB state fits the 256 MB Infinity Cache, so repeated steps can "
                 "exceed the HBM rate",
+    }
+    del qs, ks, vs, S, S0
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode_tokens(args, torch, la, la_inputs):
+    """Multi-token decode: K = 4 new tokens per (b, h) per call on the B=64,
+    H=32, d=128 decode state, 250 consecutive calls with fresh q, k, v."""
+    B, H, d, K, calls = 64, 32, 128, 4, 250
+    dev = torch.device("cuda:0")
+    slope = torch.from_numpy(la_inputs.slopes(H)).to(dev)
+    S0 = torch.from_numpy(la_inputs.decode_state(3, B, H, d)).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(33)
+    scale = 1.0 / d ** 0.5
+    qs, ks, vs = (
+        (torch.randn((calls, B, H, K, d), generator=g, device=dev) * scale).to(torch.bfloat16)
+        for _ in range(3)
+    )
+    o = torch.empty((B, H, K, d), dtype=torch.bfloat16, device=dev)
+    S = S0.clone()
+    stream = torch.cuda.current_stream()
+    for i in range(10):
+        la.decode_tokens(qs[i], ks[i], vs[i], slope, S, out=o, stream=stream)
+    S.copy_(S0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(calls):
+        la.decode_tokens(qs[i], ks[i], vs[i], slope, S, out=o, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    bytes_ = 2 * B * H * d * d * 4 + 4 * B * H * K * d * 2
+    achieved = bytes_ / (us * 1e-6) / 1e9
+    res = {
+        "B": B, "H": H, "d": d, "K": K, "calls": calls,
+        "us_per_call": us,
+        "tokens_per_s": B * K / (us * 1e-6),
+        "roofline": {"kernel": "fwd_bf16_kernel<32,128> (la_decode_tokens)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "bytes_per_launch": bytes_},
     }
     del qs, ks, vs, S, S0
     torch.cuda.empty_cache()
@@ -388,6 +433,9 @@ def main():
         log("decode B=64 ...")
         out["decode"] = bench_decode(args, torch, la, la_inputs)
         log("  %.2f us/step" % out["decode"]["us_per_step"])
+        log("decode 4 tokens per call, B=64 ...")
+        out["decode_tokens"] = bench_decode_tokens(args, torch, la, la_inputs)
+        log("  %.2f us/call" % out["decode_tokens"]["us_per_call"])
     if args.only in (None, "train"):
         log("train fwd+bwd B=4 H=16 N=32K ...")
         out["train"] = bench_train(args, torch, la, la_inputs)
@@ -422,6 +470,7 @@ def main():
         "cpu_baseline": cpu,
         "prefill": p,
         "decode": out.get("decode"),
+        "decode_tokens": out.get("decode_tokens"),
         "train": out.get("train"),
         "varlen": out.get("varlen"),
     }

@@ -8,6 +8,7 @@ for device memory (tensors) and streams.
 
     o, S = prefill(q, k, v, slope, chunk=128)        # q, k, v: [B, H, N, d] cuda tensors
     o    = decode_step(q1, k1, v1, slope, S)          # S updated in place
+    o    = decode_tokens(qK, kK, vK, slope, S)         # K tokens at once: [B, H, K, d]
     dq, dk, dv = prefill_bwd(q, k, v, dout, slope, chunk=64)
     o, S = prefill_varlen(q, k, v, slope, cu_seqlens, chunk=128)   # q: [H, T, d] packed
 
@@ -45,6 +46,7 @@ SIGNATURES = {
     "la_prefill_prepass": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
     "la_prefill_main": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "la_decode_step": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
+    "la_decode_tokens": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "la_prefill_bwd": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "la_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "la_prefill_varlen": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
@@ -202,6 +204,23 @@ def decode_step(q, k, v, slope, state, out=None, stream=None):
         _dev(out, "out", q.dtype), _stream(stream),
     )
     _check("la_decode_step", code)
+    return out
+
+
+def decode_tokens(q, k, v, slope, state, out=None, stream=None):
+    """K tokens per (b, h) on a carried state in one call.  q, k, v:
+    [B,H,K,d]; state: [B,H,d,d] fp32 updated in place.  Equals K decode_step
+    calls."""
+    B, H, K, d = q.shape
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    code = lib().la_decode_tokens(
+        dt, B, H, K, d, _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+        _dev(slope, "slope", torch.float32), _dev(state, "state", torch.float32),
+        _dev(out, "out", q.dtype), _stream(stream),
+    )
+    _check("la_decode_tokens", code)
     return out
 
 

@@ -353,6 +353,43 @@ la_status_t la_decode_step(la_dtype_t dt, int B, int H, int d, const void* q, co
   }
 }
 
+la_status_t la_decode_tokens(la_dtype_t dt, int B, int H, int K, int d, const void* q,
+                             const void* k, const void* v, const float* slope, float* state,
+                             void* o, void* stream) {
+  try {
+    if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_BAD_DTYPE;
+    if (B < 1 || H < 1 || K < 1 || !d_ok(dt, d)) return LA_ERR_BAD_SHAPE;
+    if (K > 128) return LA_ERR_UNSUPPORTED;
+    if ((long long)B * H * K > (1LL << 31) / 2) return LA_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !slope || !state || !o) return LA_ERR_NULL_POINTER;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) ||
+        !aligned16(o) || ((uintptr_t)slope & 3u))
+      return LA_ERR_ALIGNMENT;
+    const size_t esz = dt == LA_BF16 ? 2 : 4;
+    const size_t tb = (size_t)B * H * K * d * esz;
+    const size_t sb = (size_t)B * H * d * d * sizeof(float);
+    if (overlap(o, tb, q, tb) || overlap(o, tb, k, tb) || overlap(o, tb, v, tb) ||
+        overlap(o, tb, state, sb) || overlap(state, sb, q, tb) || overlap(state, sb, k, tb) ||
+        overlap(state, sb, v, tb))
+      return LA_ERR_ALIAS;
+    // A few tokens: the recurrence on the streamed state (vector ALU).
+    if (K <= la::kDecodeTokensMax)
+      return hip_status(la::launch_decode_tokens(dt == LA_BF16, B, H, K, d, q, k, v, slope,
+                                                 state, o, (hipStream_t)stream));
+    // More: one chunk of the prefill (the smallest chunk length that holds
+    // them), continued from and written back to the same state: one segment
+    // per row, so no workspace.
+    const int C = dt == LA_F32 ? 64 : (K <= 32 ? 32 : K <= 64 ? 64 : 128);
+    Plan pl = make_plan(dt, B, H, K, d, C);
+    if (pl.prepass) return LA_ERR_HIP;  // cannot happen: K <= C gives one segment
+    return run_main(dt,
+                    make_fwd(pl, B, H, K, d, C, q, k, v, slope, state, o, state, false, nullptr),
+                    uniform_table(), (hipStream_t)stream);
+  } catch (...) {
+    return LA_ERR_HIP;
+  }
+}
+
 la_status_t la_prefill_bwd(la_dtype_t dt, int B, int H, int N, int d, int C, const void* q,
                            const void* k, const void* v, const void* dout, const float* slope,
                            const float* state_in, void* dq, void* dk, void* dv,

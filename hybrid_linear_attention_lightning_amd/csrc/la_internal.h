@@ -124,6 +124,11 @@ hipError_t launch_scan(const ScanPass& p, const SeqTable& t, hipStream_t s);
 hipError_t launch_decode(bool bf16, int B, int H, int D, const void* q, const void* k,
                          const void* v, const float* slope, float* state, void* o,
                          hipStream_t s);
+// K <= kDecodeTokensMax tokens per (b, h) in one call, token tensors [B][H][K][D].
+constexpr int kDecodeTokensMax = 16;
+hipError_t launch_decode_tokens(bool bf16, int B, int H, int K, int D, const void* q,
+                                const void* k, const void* v, const float* slope, float* state,
+                                void* o, hipStream_t s);
 
 // Decay factors below this power of two are treated as exact zeros when a
 // segment start state is assembled from piece states: lambda^dist < 2^-kSkipLog2

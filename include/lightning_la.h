@@ -140,6 +140,29 @@ la_status_t la_decode_step(la_dtype_t dt, int B, int H, int d, const void *q,
                            float *state, void *o, void *stream);
 
 /* ------------------------------------------------------------------------ *
+ * la_decode_tokens -- K new tokens per (b, h) on a carried state, in one call:
+ * multi-token generation and the verification of K drafted tokens (the pages
+ * serve with multi-token generation, "linghe" section).  Equal to K
+ * consecutive la_decode_step calls: token j sees tokens 0..j of the call and
+ * the state, and the state advances by all K tokens.  The K tokens are
+ * evaluated as one chunk of the prefill form (matrix products for the
+ * in-call scores), so the state is read and written once instead of K times.
+ *
+ *   dt        LA_F32 or LA_BF16;  B, H >= 1;  1 <= K <= 128 (more gives
+ *             LA_ERR_UNSUPPORTED: use la_prefill with state_out = state_in)
+ *   d         as for la_prefill
+ *   q, k, v   [B][H][K][d] of dt
+ *   slope     [H] fp32
+ *   state     [B][H][d][d] fp32, read and written in place
+ *   o         [B][H][K][d] of dt, written; must not overlap q, k, v or state
+ * No workspace.  Errors as for la_decode_step.
+ * ------------------------------------------------------------------------ */
+la_status_t la_decode_tokens(la_dtype_t dt, int B, int H, int K, int d,
+                             const void *q, const void *k, const void *v,
+                             const float *slope, float *state, void *o,
+                             void *stream);
+
+/* ------------------------------------------------------------------------ *
  * la_prefill_bwd -- gradients of L = sum_t o_t . dout_t with respect to q, k
  * and v (training; the pages train the layer at up to 256K context).
  *

@@ -156,3 +156,17 @@ def test_varlen_workspace_plan():
     assert la.workspace_bytes_varlen(1, BF16, 2, 64, 64, [0, 0, 0]) == 0
     cu = (ctypes.c_int * 2)(0, 10)
     assert la.lib().la_workspace_bytes_varlen(2, BF16, 1, 64, 64, 1, cu) == ctypes.c_size_t(-1).value
+
+
+def test_decode_tokens_validation():
+    f = la.lib().la_decode_tokens
+
+    def call(dt=BF16, B=2, H=2, nk=4, d=128, q=Q, st=S_IN, o=O):
+        return f(dt, B, H, nk, d, q, K, V, SLOPE, st, o, None)
+
+    assert call(dt=3) == DTYPE
+    assert call(nk=0) == SHAPE and call(B=0) == SHAPE and call(d=100) == SHAPE
+    assert call(nk=129) == UNSUP
+    assert call(st=None) == NULLP and call(q=None) == NULLP
+    assert call(st=S_IN + 4) == ALIGN
+    assert call(o=S_IN + 64) == ALIAS and call(st=Q) == ALIAS

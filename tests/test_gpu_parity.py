@@ -192,3 +192,53 @@ def test_chunk_length_changes_only_rounding(oracle_mod):
         o, S = _run_prefill(q, k, v, s, C, "bf16")
         assert_close(o, ro, "bf16", "o C=%d" % C)
         assert_close(S, rS, "bf16", "S C=%d" % C, stored_bf16=False)
+
+
+DECODE_TOKENS_CASES = [
+    # dtype, B, H, K, d
+    ("bf16", 3, 4, 1, 128),
+    ("bf16", 2, 3, 3, 128),
+    ("bf16", 2, 3, 4, 128),
+    ("bf16", 2, 3, 8, 64),
+    ("bf16", 2, 3, 16, 128),  # largest K of the streaming kernel
+    ("bf16", 2, 2, 17, 64),  # smallest K of the chunk path
+    ("bf16", 2, 2, 33, 64),
+    ("f32", 3, 2, 7, 16),
+    ("bf16", 1, 2, 128, 128),
+    ("f32", 2, 3, 5, 64),
+    ("f32", 1, 2, 70, 32),
+]
+
+
+@pytest.mark.parametrize("dtype,B,H,K,d", DECODE_TOKENS_CASES)
+def test_decode_tokens(oracle_mod, dtype, B, H, K, d):
+    """K tokens on a carried state in one call: the oracle's prefill from that
+    state (which equals K decode steps, a pinned identity)."""
+    q, k, v = _inputs(900 + K, B, H, K, d, dtype)
+    s = la_inputs.slopes(H)
+    S0 = la_inputs.decode_state(11, B, H, d)
+    tq, tk, tv = (to_dev(x, dtype) for x in (q, k, v))
+    tS = torch.from_numpy(S0).to(device())
+    o = la.decode_tokens(tq, tk, tv, torch.from_numpy(s).to(device()), tS)
+    torch.cuda.synchronize()
+    ro, rS = oracle_mod.fwd(q, k, v, s, S0)
+    assert_close(to_host(o), ro, dtype, "o")
+    assert_close(to_host(tS), rS, dtype, "S", stored_bf16=False)
+
+
+def test_decode_tokens_equals_single_steps():
+    """Against K calls of la_decode_step on the same inputs (bf16)."""
+    B, H, K, d = 4, 8, 6, 128
+    q, k, v = _inputs(950, B, H, K, d, "bf16")
+    s = torch.from_numpy(la_inputs.slopes(H)).to(device())
+    S0 = torch.from_numpy(la_inputs.decode_state(12, B, H, d)).to(device())
+    tq, tk, tv = (to_dev(x, "bf16") for x in (q, k, v))
+    Sa = S0.clone()
+    oa = la.decode_tokens(tq, tk, tv, s, Sa)
+    Sb = S0.clone()
+    ob = torch.stack([la.decode_step(tq[:, :, j].contiguous(), tk[:, :, j].contiguous(),
+                                     tv[:, :, j].contiguous(), s, Sb) for j in range(K)], dim=2)
+    torch.cuda.synchronize()
+    ref = to_host(ob)
+    assert_close(to_host(oa), ref, "bf16", "o vs decode steps")
+    assert_close(to_host(Sa), to_host(Sb), "bf16", "S vs decode steps", stored_bf16=False)
