@@ -12,13 +12,17 @@ Attention" and "Context Parallel for Lightning Attention" sections):
 * `fwd`, `decode`, `bwd`, `fwd_chunked` call the plain C recurrent code in
   `la_oracle.c` (fp64, OpenMP over (b, h)); `fwd_varlen` and `bwd_varlen`
   apply them to each sequence of a packed batch;
-* `brute` holds the quadratic (masked-matrix) forms in numpy, for tiny sizes.
+* `brute` holds the quadratic (masked-matrix) forms in numpy, for tiny sizes;
+* `gated_group_rmsnorm` is the output epilogue (per-head RMSNorm, weight,
+  sigmoid gate) written out in numpy, and `fwd_gated` composes it with `fwd`.
 """
 from .core import (  # noqa: F401
     build,
     fwd,
     fwd_chunked,
     fwd_varlen,
+    fwd_gated,
+    gated_group_rmsnorm,
     decode,
     bwd,
     bwd_varlen,

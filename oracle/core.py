@@ -169,3 +169,26 @@ def bwd_varlen(q, k, v, dout, slope, cu_seqlens):
         r = bwd(q[None, :, a:b], k[None, :, a:b], v[None, :, a:b], g[None, :, a:b], slope)
         dq[:, a:b], dk[:, a:b], dv[:, a:b] = (x[0] for x in r)
     return dq, dk, dv
+
+
+def gated_group_rmsnorm(o, gate, weight, eps):
+    """The output epilogue of the "linghe" section (Group RMSNorm + Sigmoid
+    Gate), one group per head:
+
+        y[..., h, t, j] = o[..., h, t, j] / sqrt(mean_j' o[..., h, t, j']^2 + eps)
+                          * weight[h, j] * sigmoid(gate[..., h, t, j])
+
+    o, gate: [..., H, N, d]; weight: [H, d]; all in float64."""
+    o, g = _f64(o), _f64(gate)
+    w = np.asarray(weight, dtype=np.float64)
+    assert g.shape == o.shape and w.shape == o.shape[-3:-2] + o.shape[-1:]
+    ms = np.mean(o * o, axis=-1, keepdims=True)
+    sig = 1.0 / (1.0 + np.exp(-g))
+    return o / np.sqrt(ms + float(eps)) * w[:, None, :] * sig
+
+
+def fwd_gated(q, k, v, slope, gate, weight, eps, S0=None):
+    """Forward followed by the gated group RMSNorm of its output.  Returns
+    (y [B,H,N,d], S_N [B,H,d,d])."""
+    o, S = fwd(q, k, v, slope, S0)
+    return gated_group_rmsnorm(o, gate, weight, eps), S

@@ -8,7 +8,8 @@ pages describe ("Context Parallel for Lightning Attention": local recursion plus
 a global correction) and central finite differences for the backward.  Packed
 (varlen) batches are pinned to the block-diagonal masked-matrix form, to
 prefix caching (continuing from a cached state) and to the independence of
-the sequences.
+the sequences.  The output epilogue (gated group RMSNorm) is pinned to a
+hand-computed example, closed-form properties and scipy's logistic function.
 """
 import numpy as np
 import pytest
@@ -319,6 +320,59 @@ def test_varlen_backward_finite_differences(oracle_mod):
             lm = np.sum(oracle_mod.fwd_varlen(*xs, s, cu)[0] * g)
             fd = (lp - lm) / (2 * eps)
             assert abs(fd - grads[which][ix]) < 1e-6 * max(1.0, np.max(np.abs(grads[which])))
+
+
+# ------------------------------------------------------------- output epilogue
+def test_gated_norm_worked_example(oracle_mod):
+    """By hand, one token of one head, d = 2: o = (3, 4) has mean square
+    12.5; with eps = 0, weight (1, 2) and gate (0, ln 3):
+    y = (3, 4) / sqrt(12.5) * (1, 2) * (1/2, 3/4) = (0.42426..., 1.69705...)."""
+    o = np.array([[[[3.0, 4.0]]]])
+    g = np.array([[[[0.0, np.log(3.0)]]]])
+    w = np.array([[1.0, 2.0]])
+    y = oracle_mod.gated_group_rmsnorm(o, g, w, 0.0)
+    r = np.sqrt(12.5)
+    np.testing.assert_allclose(y[0, 0, 0], [3 / r * 0.5, 4 / r * 2 * 0.75], rtol=1e-15)
+
+
+def test_gated_norm_properties(oracle_mod):
+    rng = _rng(50)
+    B, H, N, d = 2, 3, 7, 16
+    o = _rand(rng, B, H, N, d)
+    g = _rand(rng, B, H, N, d, scale=2.0)
+    w = _rand(rng, H, d)
+    eps = 1e-5
+    y = oracle_mod.gated_group_rmsnorm(o, g, w, eps)
+    # a huge gate passes the normalised row through: unit RMS up to eps
+    big = np.full_like(g, 60.0)
+    yu = oracle_mod.gated_group_rmsnorm(o, big, np.ones((H, d)), eps)
+    ms = np.mean(o * o, axis=-1)
+    np.testing.assert_allclose(np.mean(yu * yu, axis=-1), ms / (ms + eps), rtol=1e-12)
+    # gate 0 halves it
+    y0 = oracle_mod.gated_group_rmsnorm(o, np.zeros_like(g), np.ones((H, d)), eps)
+    np.testing.assert_allclose(y0, 0.5 * yu, rtol=1e-12)
+    # with eps = 0 the result is invariant to scaling a row by c > 0 and odd in o
+    y1 = oracle_mod.gated_group_rmsnorm(o, g, w, 0.0)
+    y2 = oracle_mod.gated_group_rmsnorm(-7.5 * o, g, w, 0.0)
+    np.testing.assert_allclose(y2, -y1, rtol=1e-12)
+    # the gate is the logistic function (scipy's expit), the weight per (head, channel)
+    from scipy.special import expit
+    h, j = 2, 5
+    ref = o[..., h, :, j] / np.sqrt(np.mean(o[..., h, :, :] ** 2, axis=-1) + eps) * w[h, j] * expit(g[..., h, :, j])
+    np.testing.assert_allclose(y[..., h, :, j], ref, rtol=1e-12)
+
+
+def test_fwd_gated_composes(oracle_mod):
+    rng = _rng(51)
+    B, H, N, d = 1, 2, 20, 8
+    q, k, v, g = (_rand(rng, B, H, N, d) for _ in range(4))
+    w = _rand(rng, H, d)
+    s = np.array([0.1, 0.5], dtype=np.float32)
+    y, S = oracle_mod.fwd_gated(q, k, v, s, g, w, 1e-6)
+    ob, Sb = oracle_mod.brute.fwd(q, k, v, s)
+    ms = np.mean(ob * ob, axis=-1, keepdims=True)
+    assert _relerr(y, ob / np.sqrt(ms + 1e-6) * w[:, None, :] / (1 + np.exp(-g))) < 1e-12
+    assert _relerr(S, Sb) < 1e-12
 
 
 # ---------------------------------------------------------------------- backward
