@@ -9,6 +9,8 @@ sequence, inputs resident in HBM.  The same line carries:
     its HIP-event-timed average duration, against 8 TB/s;
   * "decode": the batched decode step (B=64, H=32, d=128), 1000 consecutive
     steps with fresh q/k/v each, microseconds per step and HBM fraction;
+  * "prefill_gated": the same prefill with the fused output epilogue
+    (per-head RMSNorm, weight, sigmoid gate);
   * "decode_tokens": 4 new tokens per (b, h) per call on the same state
     (multi-token generation / draft verification), microseconds per call;
   * "train": forward + backward at B=4, H=16, N=32768, d=128, chunk 64;
@@ -156,6 +158,49 @@ def bench_prefill(args, torch, la, la_inputs):
         "workspace_bytes": nws,
     }
     del q, k, v, o, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_prefill_gated(args, torch, la, la_inputs):
+    """The 128K prefill with the fused output epilogue (per-head RMSNorm,
+    weight, sigmoid gate): whole la_prefill_gated calls."""
+    c = la_inputs.CONFIGS["prefill_128k"]
+    B, H, N, d, C = c["B"], c["H"], c["N"], c["d"], c["C"]
+    dev = torch.device("cuda:0")
+    q, k, v = la_inputs.qkv_device(c["seed"], B, H, N, d, dev, torch.bfloat16)
+    gate = la_inputs.gate_device(c["seed"], B, H, N, d, dev, torch.bfloat16)
+    w = torch.from_numpy(la_inputs.norm_weight(c["seed"], H, d)).to(dev)
+    slope = torch.from_numpy(la_inputs.slopes(H)).to(dev)
+    y = torch.empty_like(q)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    nws = la.workspace_bytes(0, la.LA_BF16, B, H, N, d, C)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        la.prefill_gated(q, k, v, slope, gate, w, eps=1e-6, chunk=C, out=y, state_out=S,
+                         workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    bytes_ = prefill_counts(B, H, N, d, C)[0] + B * H * N * d * 2  # + the gate read
+    res = {
+        "B": B, "H": H, "N": N, "d": d, "C": C,
+        "ms_per_step": ms,
+        "tokens_per_s": B * N / (ms * 1e-3),
+        "hbm_frac_whole_call": bytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "note": "bytes: q, k, v, gate read, y written, final state written",
+    }
+    del q, k, v, gate, y, ws
     torch.cuda.empty_cache()
     return res
 
@@ -429,6 +474,9 @@ def main():
         log("prefill 128K ...")
         out["prefill"] = bench_prefill(args, torch, la, la_inputs)
         log("  %.3f ms/step" % out["prefill"]["ms_per_step"])
+        log("prefill 128K with the fused output epilogue ...")
+        out["prefill_gated"] = bench_prefill_gated(args, torch, la, la_inputs)
+        log("  %.3f ms/step" % out["prefill_gated"]["ms_per_step"])
     if args.only in (None, "decode"):
         log("decode B=64 ...")
         out["decode"] = bench_decode(args, torch, la, la_inputs)
@@ -469,6 +517,7 @@ def main():
         "roofline": p["roofline"] if p else None,
         "cpu_baseline": cpu,
         "prefill": p,
+        "prefill_gated": out.get("prefill_gated"),
         "decode": out.get("decode"),
         "decode_tokens": out.get("decode_tokens"),
         "train": out.get("train"),

@@ -44,6 +44,8 @@ _P, _I, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 SIGNATURES = {
     "la_prefill": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "la_prefill_prepass": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
+    "la_prefill_gated": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                              _P, _P, _P, _Z, _P]),
     "la_prefill_main": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "la_decode_step": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "la_decode_tokens": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
@@ -153,6 +155,36 @@ def prefill(q, k, v, slope, chunk=64, state_in=None, out=None, state_out=None,
         None if ws is None else ws.data_ptr(), wsb, _stream(stream),
     )
     _check("la_prefill", code)
+    return out, state_out
+
+
+def prefill_gated(q, k, v, slope, gate, norm_weight, eps=1e-6, chunk=64, state_in=None,
+                  out=None, state_out=None, return_state=True, workspace=None, stream=None):
+    """prefill with the fused output epilogue: y = RMSNorm_head(o) * norm_weight[h]
+    * sigmoid(gate), gate like q, norm_weight [H, d] fp32.  Returns (y, state_out)."""
+    B, H, N, d = q.shape
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v), ("gate", gate)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("%s must match q in shape and dtype" % name)
+    if tuple(norm_weight.shape) != (H, d):
+        raise ValueError("norm_weight must be [H, d]")
+    if out is None:
+        out = torch.empty_like(q)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    nbytes = workspace_bytes(0, dt, B, H, N, d, chunk)
+    ws, wsb = _workspace(nbytes, q.device, workspace)
+    code = lib().la_prefill_gated(
+        dt, B, H, N, d, chunk,
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(slope, "slope", torch.float32),
+        None if state_in is None else _dev(state_in, "state_in", torch.float32),
+        _dev(gate, "gate", q.dtype), _dev(norm_weight, "norm_weight", torch.float32), float(eps),
+        _dev(out, "out", q.dtype),
+        None if state_out is None else _dev(state_out, "state_out", torch.float32),
+        None if ws is None else ws.data_ptr(), wsb, _stream(stream),
+    )
+    _check("la_prefill_gated", code)
     return out, state_out
 
 

@@ -295,6 +295,40 @@ la_status_t la_prefill(la_dtype_t dt, int B, int H, int N, int d, int C, const v
   }
 }
 
+la_status_t la_prefill_gated(la_dtype_t dt, int B, int H, int N, int d, int C, const void* q,
+                             const void* k, const void* v, const float* slope,
+                             const float* state_in, const void* gate, const float* norm_weight,
+                             float eps, void* y, float* state_out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  try {
+    Plan pl;
+    const la_status_t st = check_prefill(dt, B, H, N, d, C, q, k, v, slope, state_in, y,
+                                         state_out, workspace, workspace_bytes, true, &pl);
+    if (st != LA_OK) return st;
+    if (!gate || !norm_weight) return LA_ERR_NULL_POINTER;
+    if (!aligned16(gate) || ((uintptr_t)norm_weight & 3u)) return LA_ERR_ALIGNMENT;
+    if (!(eps >= 0.f) || eps > 3.0e38f) return LA_ERR_BAD_SHAPE;  // also rejects NaN
+    const size_t esz = dt == LA_BF16 ? 2 : 4;
+    const size_t tb = (size_t)B * H * N * d * esz;
+    if (overlap(y, tb, gate, tb) || overlap(y, tb, norm_weight, (size_t)H * d * sizeof(float)))
+      return LA_ERR_ALIAS;
+    if (state_out && (overlap(state_out, (size_t)B * H * d * d * sizeof(float), gate, tb)))
+      return LA_ERR_ALIAS;
+    const hipStream_t s = (hipStream_t)stream;
+    la_status_t r = run_prepass(pl, uniform_table(), B, H, N, d, C, k, v, slope, state_in, false,
+                                workspace, s);
+    if (r != LA_OK) return r;
+    la::FwdPass fp = make_fwd(pl, B, H, N, d, C, q, k, v, slope, state_in, y, state_out, false,
+                              workspace);
+    fp.gate = gate;
+    fp.norm_w = norm_weight;
+    fp.eps = eps;
+    return run_main(dt, fp, uniform_table(), s);
+  } catch (...) {
+    return LA_ERR_HIP;
+  }
+}
+
 la_status_t la_prefill_prepass(la_dtype_t dt, int B, int H, int N, int d, int C, const void* k,
                                const void* v, const float* slope, const float* state_in,
                                void* workspace, size_t workspace_bytes, void* stream) {

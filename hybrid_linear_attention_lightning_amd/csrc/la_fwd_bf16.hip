@@ -73,7 +73,8 @@ struct Cfg {
   static_assert(D == 64 || D == 128, "head dim");
   static_assert((RPI * NW) % 16 == 0, "row mod 16 per lane");
   static_assert(C % (RPI * NW) == 0, "whole direct moves per wave");
-  static_assert((STATE_ONLY ? 4 * TILE : 3 * TILE + 2 * PT_HALF) * 2 <= 160 * 1024, "LDS");
+  static_assert((STATE_ONLY ? 4 * TILE : 3 * TILE + 2 * PT_HALF) * 2 + 4 * NW * C <= 160 * 1024,
+                "LDS");
 };
 
 // Swizzle of the 16-byte chunk index of row r of a [C][D] bf16 tile.  It
@@ -88,9 +89,12 @@ __host__ __device__ constexpr int swz_of(int r) {
   return ((r >> 1) & 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 1) | (((r >> 3) & 1) << 2);
 }
 
-template <int C, int D, bool STATE_ONLY>
+// EPI: the output epilogue (per-head RMSNorm, per-channel weight, sigmoid
+// gate) is applied to the fp32 outputs before they are rounded and stored.
+template <int C, int D, bool STATE_ONLY, bool EPI>
 __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PiecePass pp,
                                                                 const SeqTable st) {
+  static_assert(!(STATE_ONLY && EPI), "the epilogue belongs to the main pass");
   using G = Cfg<C, D, STATE_ONLY>;
   constexpr int kThreads = G::THREADS;
   constexpr int CT = G::CT;
@@ -108,7 +112,7 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
   int tau0, tau_end;
   bool reverse;
   const float* slope;
-  const uint16_t *qg = nullptr, *kg, *vg;
+  const uint16_t *qg = nullptr, *kg, *vg, *gg = nullptr;
   uint16_t* og = nullptr;
   const float* s_init = nullptr;
   float* s_final = nullptr;
@@ -172,6 +176,7 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
     kg = (const uint16_t*)p.k + head_off;
     vg = (const uint16_t*)p.v + head_off;
     og = (uint16_t*)p.o + head_off;
+    if constexpr (EPI) gg = (const uint16_t*)p.gate + head_off;
     if (seg == 0)
       s_init = p.state_in ? p.state_in + (size_t)row.st * D * D : nullptr;
     else
@@ -467,6 +472,19 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
   } else {
     __shared__ __attribute__((aligned(16))) uint16_t Ks[G::TILE], Vs[G::TILE], Qs[G::TILE],
         Pth[G::PT_HALF], Ptl[G::PT_HALF];
+    // epilogue: per-wave partial sums of squares of each output row, the
+    // norm weights of this lane's columns (col0 + 16ct + 4lg + r) and the eps
+    __shared__ float ssq[EPI ? G::NW : 1][EPI ? C : 1];
+    float wn[EPI ? CT : 1][4];
+    float eps = 0.f;
+    if constexpr (EPI) {
+      eps = p.eps;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          wn[ct][r] = p.norm_w[(size_t)row.h * D + col0 + 16 * ct + 4 * lg + r];
+    }
     // All three tiles move straight from HBM to LDS.  Per chunk: K and V
     // (issued during the previous chunk's outputs) feed the state update,
     // which gives Q (issued last, once the previous outputs are done with
@@ -507,7 +525,24 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
 
       state_update(Ks, vf, n);
 
-      wait_vmcnt<0>();
+      // epilogue: this lane's gate values (rows 16qb + li, columns col0 +
+      // 16ct + 4lg .. +3).  Issued after Q's moves and before the next
+      // chunk's K and V (vector-memory operations complete in order), they
+      // land during the score tiles without delaying either.
+      constexpr int kGateLoads = EPI ? G::NQB * CT : 0;
+      u32x2_t gq[EPI ? G::NQB : 1][CT];
+      if constexpr (EPI) {
+        const uint16_t* gb = gg + (long)tc * D + col0 + 4 * lg;
+#pragma unroll
+        for (int qb = 0; qb < G::NQB; ++qb) {
+          const int rr = min(16 * qb + li, n - 1);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            gq[qb][ct] = *reinterpret_cast<const u32x2_t*>(gb + rr * D + 16 * ct);
+        }
+      }
+
+      wait_vmcnt<kGateLoads>();  // Q's moves (issued before the gate loads) are done
       lds_barrier();  // Q of chunk tc is in LDS
 
       // ---- masked scores P^T = (K Q^T) * M^T -> LDS as hi/lo B fragments ----
@@ -578,7 +613,90 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
       const int li_c = opaque(li);
       const int o_lane = 4 * lg + (reverse ? (n - 1 - li_c) : li_c) * D;
       const int o_qb = reverse ? -16 * D : 16 * D;
-      // a full chunk stores every row: its output loop has no branches
+      // epilogue: gated, weighted rows held until every wave's sums of squares
+      // are in LDS
+      f32x4_t z[EPI ? G::NQB : 1][CT];
+      // finished rows of query block qb: stored, or (epilogue) gated and
+      // weighted and their sums of squares handed to LDS
+      auto tail = [&](int qb, const f32x4_t (&acc)[CT], bool store) __attribute__((always_inline)) {
+        if constexpr (EPI) {
+          float ss = 0.f;
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              ss = fmaf(acc[ct][r], acc[ct][r], ss);
+              const uint32_t gw = gq[qb][ct][r >> 1];
+              const float g = (r & 1) ? bf_hi(gw) : bf_lo(gw);
+              const float sig = __builtin_amdgcn_rcpf(1.f + fast_exp2(-kLog2e * g));
+              z[qb][ct][r] = acc[ct][r] * wn[ct][r] * sig;
+            }
+          // the row's 32 columns of this wave sit in the 4 lane groups
+          ss = sum_lane_xor32(sum_lane_xor16(ss));
+          if (lg == 0) ssq[wave][16 * qb + li] = ss;
+        } else if (store) {
+          uint16_t* dst = obase + (o_lane + qb * o_qb);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            *reinterpret_cast<u32x2_t*>(dst + 16 * ct) =
+                u32x2_t{pack2(acc[ct][0], acc[ct][1]), pack2(acc[ct][2], acc[ct][3])};
+        }
+      };
+      // Full chunk, software-pipelined over query blocks: block qb's Q^T
+      // fragments were read during block qb-1; its own P^T fragments are
+      // read first and land during its 16 inter-chunk products; the tail of
+      // block qb-1 runs between block qb's products.
+      auto outputs_full = [&]() __attribute__((always_inline)) {
+        u32x4_t qf[2][G::KSD];
+#pragma unroll
+        for (int ks = 0; ks < G::KSD; ++ks) qf[0][ks] = lds_read16(Qs + lA[ks]);
+        f32x4_t hold[CT];
+#pragma unroll
+        for (int qb = 0; qb < G::NQB; ++qb) {
+          const int b = qb & 1;
+          u32x4_t pfh[G::KSC], pfl[G::KSC];
+#pragma unroll
+          for (int ks = 0; ks <= qb / 2; ++ks) {
+            pfh[ks] = lds_read16(Pth + (frag_base(qb) + ks) * 512 + 8 * lane);
+            pfl[ks] = lds_read16(Ptl + (frag_base(qb) + ks) * 512 + 8 * lane);
+          }
+          if (qb + 1 < G::NQB) {
+#pragma unroll
+            for (int ks = 0; ks < G::KSD; ++ks)
+              qf[b ^ 1][ks] = lds_read16(Qs + 16 * (qb + 1) * D + lA[ks]);
+          }
+          f32x4_t x[CT], a[CT];
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            x[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            a[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int ks = 0; ks < G::KSD; ++ks)
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+              for (int ct = 0; ct < CT; ++ct)
+                x[ct] = mfma16(hl ? sfl[ct][ks] : sfh[ct][ks], qf[b][ks], x[ct]);
+#pragma unroll
+          for (int ks = 0; ks <= qb / 2; ++ks)
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+              for (int ct = 0; ct < CT; ++ct)
+                a[ct] = mfma16(vf[ks][ct], hl ? pfl[ks] : pfh[ks], a[ct]);
+          if (qb > 0) tail(qb - 1, hold, true);
+          __builtin_amdgcn_sched_barrier(0);
+          const float aq = a_lane * fast_exp2(-sl2 * (float)(16 * qb));
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hold[ct][r] = fmaf(aq, x[ct][r], a[ct][r]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        tail(G::NQB - 1, hold, true);
+      };
+      // partial chunk (the last of a sequence): straightforward order
       auto outputs = [&](auto full_c) {
         constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
@@ -611,20 +729,34 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
               acc[ct] = mfma16(vf[ks][ct], pfl[ks], acc[ct]);
             }
           }
-          if (FULL || 16 * qb + li_c < n) {
+          tail(qb, acc, FULL || 16 * qb + li_c < n);
+        }
+      };
+      if (n == C)
+        outputs_full();
+      else
+        outputs(std::false_type{});
+      lds_barrier();  // Q and P^T tiles are free for the next chunk
+      if constexpr (EPI) {
+        // every wave's sums of squares are in: scale the held rows
+#pragma unroll
+        for (int qb = 0; qb < G::NQB; ++qb) {
+          float tot = 0.f;
+#pragma unroll
+          for (int w = 0; w < G::NW; ++w) tot += ssq[w][16 * qb + li];
+          const float rn = __builtin_amdgcn_rsqf(tot * (1.f / D) + eps);
+          if (16 * qb + li_c < n) {
             uint16_t* dst = obase + (o_lane + qb * o_qb);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
               *reinterpret_cast<u32x2_t*>(dst + 16 * ct) =
-                  u32x2_t{pack2(acc[ct][0], acc[ct][1]), pack2(acc[ct][2], acc[ct][3])};
+                  u32x2_t{pack2(z[qb][ct][0] * rn, z[qb][ct][1] * rn),
+                          pack2(z[qb][ct][2] * rn, z[qb][ct][3] * rn)};
           }
         }
-      };
-      if (n == C)
-        outputs(std::true_type{});
-      else
-        outputs(std::false_type{});
-      lds_barrier();  // Q and P^T tiles are free for the next chunk
+      }
+      // after the epilogue's stores, so that the next chunk's wait for its K
+      // and V (all but Q's moves) does not wait for Q
       if (more) load_direct(qg, Qs, tc + C, n_next);
     }
   }
@@ -644,8 +776,12 @@ template <int C, int D>
 hipError_t launch_fwd_cd(const FwdPass& p, const SeqTable& t, hipStream_t s) {
   PiecePass none{};
   const unsigned grid = (unsigned)(t.nseq > 0 ? p.H * p.G : p.B * p.H * p.nseg);
-  hipLaunchKernelGGL((fwd_bf16_kernel<C, D, false>), dim3(grid), dim3(D / 32 * 64), 0, s, p, none,
-                     t);
+  if (p.gate)
+    hipLaunchKernelGGL((fwd_bf16_kernel<C, D, false, true>), dim3(grid), dim3(D / 32 * 64), 0, s,
+                       p, none, t);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<C, D, false, false>), dim3(grid), dim3(D / 32 * 64), 0,
+                       s, p, none, t);
   return hipGetLastError();
 }
 
@@ -654,8 +790,8 @@ hipError_t launch_pieces_cd(const PiecePass& pp, const SeqTable& t, hipStream_t 
   FwdPass none{};
   const unsigned grid = (unsigned)(t.nseq > 0 ? pp.H * pp.G * (pp.seg_len / pp.piece_len)
                                               : pp.B * pp.H * pp.npiece);
-  hipLaunchKernelGGL((fwd_bf16_kernel<C, D, true>), dim3(grid), dim3(D / 32 * 64), 0, s, none, pp,
-                     t);
+  hipLaunchKernelGGL((fwd_bf16_kernel<C, D, true, false>), dim3(grid), dim3(D / 32 * 64), 0, s,
+                     none, pp, t);
   return hipGetLastError();
 }
 

@@ -49,6 +49,11 @@ struct FwdPass {
   int nseg;
   int G;
   const float* seg_states;  // [B][H][nseg][D][D] / [H][G][D][D], or nullptr
+  // Output epilogue (forward only), when gate != nullptr:
+  // o = RMSNorm_head(o) * norm_w[h] * sigmoid(gate), gate laid out like o.
+  const void* gate;
+  const float* norm_w;  // [H][D]
+  float eps;
 };
 
 // Per-piece local states for the segment pre-pass:

@@ -71,13 +71,16 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanPass p, const SeqTable st
   }
 }
 
-template <int D, int CS>
+// EPI: the output epilogue (per-head RMSNorm, per-channel weight, sigmoid
+// gate) on each block's fp32 output rows, staged in LDS, before the store.
+template <int D, int CS, bool EPI>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdPass p, const SeqTable st) {
   constexpr int DS = D + 1;  // padded row stride
   __shared__ float Sm[D * D];
   __shared__ float Qm[CS * DS], Km[CS * DS], Vm[CS * DS];
   __shared__ float Pm[CS * (CS + 1)];
   __shared__ float bj[CS];
+  __shared__ float Om[EPI ? CS * DS : 1], rn[EPI ? CS : 1];
   const int tid = threadIdx.x;
   // one (sequence, head) row per workgroup
   const Row row = st.nseq > 0 ? packed_row(st, blockIdx.x / p.H, blockIdx.x % p.H, p.H, 0, 0)
@@ -120,9 +123,29 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdPass p, const SeqTable 
       float intra = 0.f, inter = 0.f;
       for (int j = 0; j <= i; ++j) intra = fmaf(Pm[i * (CS + 1) + j], Vm[j * DS + c], intra);
       for (int x = 0; x < D; ++x) inter = fmaf(Qm[i * DS + x], Sm[x * D + c], inter);
-      og[(size_t)tok(t0 + i) * D + c] = intra + exp2f(-sl2 * (float)(i + 1)) * inter;
+      const float out = intra + exp2f(-sl2 * (float)(i + 1)) * inter;
+      if constexpr (EPI)
+        Om[i * DS + c] = out;
+      else
+        og[(size_t)tok(t0 + i) * D + c] = out;
     }
     __syncthreads();
+    if constexpr (EPI) {
+      const float* gt = (const float*)p.gate + head_off;
+      if (tid < n) {
+        float ss = 0.f;
+        for (int c = 0; c < D; ++c) ss = fmaf(Om[tid * DS + c], Om[tid * DS + c], ss);
+        rn[tid] = 1.f / sqrtf(ss / (float)D + p.eps);
+      }
+      __syncthreads();
+      for (int e = tid; e < CS * D; e += 256) {
+        const int i = e / D, c = e % D;
+        if (i >= n) continue;
+        const size_t g = (size_t)tok(t0 + i) * D + c;
+        const float sig = 1.f / (1.f + expf(-gt[g]));
+        og[g] = Om[i * DS + c] * rn[i] * p.norm_w[(size_t)row.h * D + c] * sig;
+      }
+    }
     const float g = exp2f(-sl2 * (float)n);
     if (tid < CS) bj[tid] = tid < n ? exp2f(-sl2 * (float)(n - 1 - tid)) : 0.f;
     __syncthreads();
@@ -141,7 +164,10 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdPass p, const SeqTable 
 template <int D, int CS>
 hipError_t launch_f32(const FwdPass& p, const SeqTable& t, hipStream_t s) {
   const unsigned grid = (unsigned)((t.nseq > 0 ? t.nseq : p.B) * p.H);
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CS>), dim3(grid), dim3(256), 0, s, p, t);
+  if (p.gate)
+    hipLaunchKernelGGL((fwd_f32_kernel<D, CS, true>), dim3(grid), dim3(256), 0, s, p, t);
+  else
+    hipLaunchKernelGGL((fwd_f32_kernel<D, CS, false>), dim3(grid), dim3(256), 0, s, p, t);
   return hipGetLastError();
 }
 

@@ -95,6 +95,32 @@ la_status_t la_prefill(la_dtype_t dt, int B, int H, int N, int d, int C,
                        size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------ *
+ * la_prefill_gated -- la_prefill with the layer's output epilogue fused in:
+ * the Group RMSNorm + Sigmoid Gate that the pages fuse for inference
+ * ("linghe" section), one group per head.  For every token t and head h,
+ * with x = o_t (the d outputs of la_prefill, in fp32, before rounding):
+ *
+ *     y_t[j] = x[j] / sqrt(mean_j' x[j']^2 + eps) * norm_weight[h][j]
+ *              * sigmoid(gate_t[j])
+ *
+ * and y is written instead of o (rounded once, to dt).  The norm sees the
+ * whole head row, so o never makes a round trip through memory.
+ *
+ *   arguments of la_prefill, with o replaced by y, plus
+ *   gate         [B][H][N][d] of dt, 16-byte aligned, must not overlap y
+ *   norm_weight  [H][d] fp32
+ *   eps          finite, >= 0 (LA_ERR_BAD_SHAPE otherwise)
+ *   workspace    at least la_workspace_bytes(0, ...) bytes
+ * ------------------------------------------------------------------------ */
+la_status_t la_prefill_gated(la_dtype_t dt, int B, int H, int N, int d, int C,
+                             const void *q, const void *k, const void *v,
+                             const float *slope, const float *state_in,
+                             const void *gate, const float *norm_weight,
+                             float eps, void *y, float *state_out,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* ------------------------------------------------------------------------ *
  * la_prefill_prepass / la_prefill_main -- la_prefill in two calls.
  *
  * When B*H is small, la_prefill cuts each sequence into segments that run in

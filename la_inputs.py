@@ -14,7 +14,9 @@ synthetic stand-ins documented in the design doc):
   * per-head slope s_h = 2^(-8 (h+1) / H), h = 0..H-1, so the decay is
     lambda_h = exp(-s_h);
   * packed (varlen) batches: sequence boundaries at nseq - 1 distinct cut
-    points drawn uniformly over the packed tokens.
+    points drawn uniformly over the packed tokens;
+  * output epilogue: gate pre-activations ~ N(0, 1), RMSNorm weights
+    1 + N(0, 0.1^2) per (head, channel), eps = 1e-6.
 
 Each tensor draws from numpy.random.default_rng([seed, tensor_id, step]), so a
 tensor never depends on the sizes of the tensors drawn before it.
@@ -25,6 +27,7 @@ import numpy as np
 
 # tensor ids for the seed sequence
 Q_ID, K_ID, V_ID, DO_ID, S0_ID = 1, 2, 3, 4, 5
+GATE_ID, NORMW_ID = 7, 8
 
 
 def slopes(H: int) -> np.ndarray:
@@ -67,6 +70,25 @@ def upstream_grad(seed: int, B: int, H: int, N: int, d: int, dtype: str = "bf16"
     """dO of shape [B,H,N,d] ~ N(0,1)."""
     x = _normal(seed, DO_ID, 0, (B, H, N, d), 1.0)
     return bf16_round(x) if dtype == "bf16" else x
+
+
+def gate(seed: int, B: int, H: int, N: int, d: int, dtype: str = "bf16"):
+    """Output-gate pre-activations of shape [B,H,N,d] ~ N(0,1)."""
+    x = _normal(seed, GATE_ID, 0, (B, H, N, d), 1.0)
+    return bf16_round(x) if dtype == "bf16" else x
+
+
+def norm_weight(seed: int, H: int, d: int) -> np.ndarray:
+    """Per-(head, channel) RMSNorm weights [H,d] fp32, 1 + N(0, 0.1^2)."""
+    return (1.0 + _normal(seed, NORMW_ID, 0, (H, d), 0.1)).astype(np.float32)
+
+
+def gate_device(seed: int, B: int, H: int, N: int, d: int, device, torch_dtype):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 1000003 + GATE_ID)
+    return torch.randn((B, H, N, d), generator=g, device=device, dtype=torch.float32).to(torch_dtype)
 
 
 def decode_state(seed: int, B: int, H: int, d: int) -> np.ndarray:

@@ -170,3 +170,20 @@ def test_decode_tokens_validation():
     assert call(st=None) == NULLP and call(q=None) == NULLP
     assert call(st=S_IN + 4) == ALIGN
     assert call(o=S_IN + 64) == ALIAS and call(st=Q) == ALIAS
+
+
+def test_gated_prefill_validation():
+    f = la.lib().la_prefill_gated
+    G, W = 0x10_0000_0000 * 20, 0x10_0000_0000 * 21
+    nws = la.workspace_bytes(0, BF16, 1, 2, 256, 128, 64)
+
+    def call(gate=G, w=W, eps=1e-6, y=O, ws=WSP, wsb=nws):
+        return f(BF16, 1, 2, 256, 128, 64, Q, K, V, SLOPE, None, gate, w, eps, y, None, ws, wsb,
+                 None)
+
+    assert call(gate=None) == NULLP and call(w=None) == NULLP
+    assert call(gate=G + 8) == ALIGN and call(w=W + 2) == ALIGN
+    assert call(eps=-1.0) == SHAPE and call(eps=float("nan")) == SHAPE
+    assert call(eps=float("inf")) == SHAPE
+    assert call(y=G) == ALIAS and call(y=W) == ALIAS
+    assert call(ws=None, wsb=0) == WS

@@ -134,3 +134,25 @@ def test_varlen_128k_sampled_heads(oracle_mod):
         assert_close(go[i], ro[i], "bf16", "o head %d" % h)
         assert_close(gS[:, i], rS[:, i], "bf16", "S head %d" % h, stored_bf16=False)
     assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+
+
+def test_prefill_gated_128k_sampled_heads(oracle_mod):
+    """The 128K prefill with the fused output epilogue, as the benchmark runs it."""
+    c = la_inputs.CONFIGS["prefill_128k"]
+    B, H, N, d, C = c["B"], c["H"], c["N"], c["d"], c["C"]
+    dev = device()
+    tq, tk, tv = la_inputs.qkv_device(c["seed"], B, H, N, d, dev, torch.bfloat16)
+    tg = la_inputs.gate_device(c["seed"], B, H, N, d, dev, torch.bfloat16)
+    w = la_inputs.norm_weight(c["seed"], H, d)
+    s = la_inputs.slopes(H)
+    y, S = la.prefill_gated(tq, tk, tv, torch.from_numpy(s).to(dev), tg,
+                            torch.from_numpy(w).to(dev), eps=1e-6, chunk=C)
+    torch.cuda.synchronize()
+    heads = [0, 31]
+    q, k, v, g = (_host(t[:, heads]) for t in (tq, tk, tv, tg))
+    ry, rS = oracle_mod.fwd_gated(q, k, v, s[heads], g, w[heads], 1e-6)
+    gy, gS = _host(y[:, heads]), _host(S[:, heads])
+    for i, h in enumerate(heads):
+        assert_close(gy[:, i], ry[:, i], "bf16", "y head %d" % h)
+        assert_close(gS[:, i], rS[:, i], "bf16", "S head %d" % h, stored_bf16=False)
+    assert torch.isfinite(y.float()).all()

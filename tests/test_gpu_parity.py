@@ -242,3 +242,34 @@ def test_decode_tokens_equals_single_steps():
     ref = to_host(ob)
     assert_close(to_host(oa), ref, "bf16", "o vs decode steps")
     assert_close(to_host(Sa), to_host(Sb), "bf16", "S vs decode steps", stored_bf16=False)
+
+
+GATED_CASES = [
+    # dtype, B, H, N, d, C, with_state
+    ("bf16", 1, 2, 1, 128, 64, False),
+    ("bf16", 1, 3, 300, 128, 128, True),
+    ("bf16", 2, 2, 200, 128, 32, False),
+    ("bf16", 1, 4, 777, 64, 64, True),
+    ("bf16", 16, 16, 70, 128, 64, False),  # 256 heads: single segment
+    ("f32", 1, 2, 100, 128, 64, True),
+    ("f32", 2, 2, 70, 32, 32, False),
+]
+
+
+@pytest.mark.parametrize("dtype,B,H,N,d,C,with_state", GATED_CASES)
+def test_prefill_gated(oracle_mod, dtype, B, H, N, d, C, with_state):
+    """The fused output epilogue (per-head RMSNorm, weight, sigmoid gate)."""
+    q, k, v = _inputs(1000 + N, B, H, N, d, dtype)
+    g = la_inputs.gate(1000 + N, B, H, N, d, dtype=dtype)
+    w = la_inputs.norm_weight(1000 + N, H, d)
+    s = la_inputs.slopes(H)
+    S0 = la_inputs.decode_state(13, B, H, d) if with_state else None
+    eps = 1e-6
+    tq, tk, tv, tg = (to_dev(x, dtype) for x in (q, k, v, g))
+    tS0 = None if S0 is None else torch.from_numpy(S0).to(device())
+    y, S = la.prefill_gated(tq, tk, tv, torch.from_numpy(s).to(device()), tg,
+                            torch.from_numpy(w).to(device()), eps=eps, chunk=C, state_in=tS0)
+    torch.cuda.synchronize()
+    ry, rS = oracle_mod.fwd_gated(q, k, v, s, g, w, eps, S0)
+    assert_close(to_host(y), ry, dtype, "y")
+    assert_close(to_host(S), rS, dtype, "S", stored_bf16=False)
