@@ -551,11 +551,13 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
       // consumer lane (2(kb&1) + (lg>>1), li).  Wave w takes the query-block
       // pairs {p, NQB-1-p}, p = w, w + NW, ...: NQB+1 tiles per pair, and each
       // K fragment serves both blocks of the pair.
-      auto score_tile = [&](const u32x4_t (&kf)[G::KSD], const u32x4_t (&qf)[G::KSD], int kb,
-                            int qb) {
+      auto score_mfma = [&](const u32x4_t (&kf)[G::KSD], const u32x4_t (&qf)[G::KSD]) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < G::KSD; ++ks) acc = mfma16(kf[ks], qf[ks], acc);
+        return acc;
+      };
+      auto score_store = [&](f32x4_t acc, int kb, int qb) {
         const int delta = qb - kb;
         if (delta == 0) {
 #pragma unroll
@@ -584,13 +586,20 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
           qfl[ks] = lds_read16(Qs + 16 * qlo * D + lA[ks]);
           qfh[ks] = lds_read16(Qs + 16 * qhi * D + lA[ks]);
         }
+        // K fragments double-buffered: key block kb+1's reads are in flight
+        // while block kb's tiles are computed
+        u32x4_t kf[2][G::KSD];
+#pragma unroll
+        for (int ks = 0; ks < G::KSD; ++ks) kf[0][ks] = lds_read16(Ks + lA[ks]);
 #pragma unroll
         for (int kb = 0; kb <= qhi; ++kb) {
-          u32x4_t kf[G::KSD];
+          if (kb + 1 <= qhi) {
 #pragma unroll
-          for (int ks = 0; ks < G::KSD; ++ks) kf[ks] = lds_read16(Ks + 16 * kb * D + lA[ks]);
-          score_tile(kf, qfh, kb, qhi);
-          if (kb <= qlo && qlo != qhi) score_tile(kf, qfl, kb, qlo);
+            for (int ks = 0; ks < G::KSD; ++ks)
+              kf[(kb + 1) & 1][ks] = lds_read16(Ks + 16 * (kb + 1) * D + lA[ks]);
+          }
+          score_store(score_mfma(kf[kb & 1], qfh), kb, qhi);
+          if (kb <= qlo && qlo != qhi) score_store(score_mfma(kf[kb & 1], qfl), kb, qlo);
         }
       };
       for (int pr = wave; pr < G::NPAIR; pr += G::NW) {
