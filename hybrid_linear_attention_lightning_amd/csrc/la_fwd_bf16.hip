@@ -58,7 +58,8 @@ template <int C, int D, bool STATE_ONLY>
 struct Cfg {
   static constexpr int NW = D / 32;    // waves: 32 value columns each
   static constexpr int THREADS = 64 * NW;
-  static constexpr int CT = 2;         // 16-column value tiles per wave
+  static constexpr int CT = 2;         // 16-column value tiles per wave (the
+                                       // output stores assume exactly two)
   static constexpr int NQB = C / 16;   // 16-token query / key blocks per chunk
   static constexpr int KSC = C / 32;   // 32-token contraction steps
   static constexpr int KSD = D / 32;   // 32-feature contraction steps
@@ -187,11 +188,15 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
   const float sl2 = slope[row.h] * kLog2e;  // lambda^e = exp2(-sl2 * e)
   const int col0 = 32 * wave;                // this wave's first value column
 
-  // ---- fp32 state: S[t][ct][r] = S[feature feat(t, r)][value col0 + 16ct + li]
+  // ---- fp32 state: S[t][ct][r] = S[feature feat(t, r)][value col0 + vcol(ct, li)]
+  // Value columns of the wave's two 16-column tiles are interleaved by 4:
+  // tile ct, row m is column 8(m>>2) + 4ct + (m&3), so that the 4 output
+  // columns a lane holds in each tile are 8 adjacent columns in all.
   // Feature order: tiles 2m and 2m+1 hold, in lane group lg, the two halves
   // of the 8 consecutive features 32m + 8lg .. +7, so that the state, split
   // into bf16 operands, meets Q in the plain row-fragment order.
   auto feat = [&](int t, int r) { return 32 * (t >> 1) + 8 * lg + 4 * (t & 1) + r; };
+  auto vcol = [&](int ct, int m) { return 8 * (m >> 2) + 4 * ct + (m & 3); };
   f32x4_t S[G::NT][CT];
 #pragma unroll
   for (int t = 0; t < G::NT; ++t)
@@ -199,7 +204,7 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        S[t][ct][r] = s_init ? s_init[(size_t)feat(t, r) * D + col0 + 16 * ct + li] : 0.f;
+        S[t][ct][r] = s_init ? s_init[(size_t)feat(t, r) * D + col0 + vcol(ct, li)] : 0.f;
 
   // ---- per-lane decay tables --------------------------------------------
   // P^T tile element: key row 16kb + 4lg + r, query column 16qb + li.
@@ -228,9 +233,9 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
   for (int ks = 0; ks < G::KSD; ++ks) offA[ks] = li * D + 8 * ((4 * ks + lg) ^ sA);
   // transposing reads: row 8lg + (li>>2) + 4hh (+32ks), 4 columns from
   // cols(li&3) on; lane i of the lane group then receives column
-  // cols(i>>2) + (i&3) of those 4 rows.  Value tiles take the columns in
-  // order (cols(j) = 16ct + 4j), K^T tiles in the state's feature order
-  // (cols(j) = feat(t, 0) of lane group j).
+  // cols(i>>2) + (i&3) of those 4 rows.  Value tiles take the interleaved
+  // value columns (cols(j) = col0 + vcol(ct, 4j)), K^T tiles the state's
+  // feature order (cols(j) = feat(t, 0) of lane group j).
   auto off_tr = [&](int hh, int chunk16, int half) {
     const int r = 8 * lg + (li >> 2) + 4 * hh;
     return r * D + 8 * (chunk16 ^ swz_of<D>(r & 15)) + 4 * half;
@@ -242,7 +247,7 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
     for (int t = 0; t < G::NT; ++t) offT[t][hh] = off_tr(hh, 4 * (t >> 1) + (li & 3), t & 1);
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
-      offV[ct][hh] = off_tr(hh, 2 * (2 * wave + ct) + ((li & 3) >> 1), li & 1);
+      offV[ct][hh] = off_tr(hh, 4 * wave + (li & 3), ct);
   }
   // The per-lane offsets are re-issued in place at the top of every chunk
   // through an empty asm, so the compiler cannot hoist the dozens of
@@ -473,7 +478,7 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
     __shared__ __attribute__((aligned(16))) uint16_t Ks[G::TILE], Vs[G::TILE], Qs[G::TILE],
         Pth[G::PT_HALF], Ptl[G::PT_HALF];
     // epilogue: per-wave partial sums of squares of each output row, the
-    // norm weights of this lane's columns (col0 + 16ct + 4lg + r) and the eps
+    // norm weights of this lane's columns (col0 + 8lg + 4ct + r) and the eps
     __shared__ float ssq[EPI ? G::NW : 1][EPI ? C : 1];
     float wn[EPI ? CT : 1][4];
     float eps = 0.f;
@@ -483,7 +488,7 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          wn[ct][r] = p.norm_w[(size_t)row.h * D + col0 + 16 * ct + 4 * lg + r];
+          wn[ct][r] = p.norm_w[(size_t)row.h * D + col0 + 8 * lg + 4 * ct + r];
     }
     // All three tiles move straight from HBM to LDS.  Per chunk: K and V
     // (issued during the previous chunk's outputs) feed the state update,
@@ -526,19 +531,17 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
       state_update(Ks, vf, n);
 
       // epilogue: this lane's gate values (rows 16qb + li, columns col0 +
-      // 16ct + 4lg .. +3).  Issued after Q's moves and before the next
+      // 8lg .. +7).  Issued after Q's moves and before the next
       // chunk's K and V (vector-memory operations complete in order), they
       // land during the score tiles without delaying either.
-      constexpr int kGateLoads = EPI ? G::NQB * CT : 0;
-      u32x2_t gq[EPI ? G::NQB : 1][CT];
+      constexpr int kGateLoads = EPI ? G::NQB : 0;
+      u32x4_t gq[EPI ? G::NQB : 1];
       if constexpr (EPI) {
-        const uint16_t* gb = gg + (long)tc * D + col0 + 4 * lg;
+        const uint16_t* gb = gg + (long)tc * D + col0 + 8 * lg;
 #pragma unroll
         for (int qb = 0; qb < G::NQB; ++qb) {
           const int rr = min(16 * qb + li, n - 1);
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct)
-            gq[qb][ct] = *reinterpret_cast<const u32x2_t*>(gb + rr * D + 16 * ct);
+          gq[qb] = *reinterpret_cast<const u32x4_t*>(gb + rr * D);
         }
       }
 
@@ -620,7 +623,7 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
       // 32-bit offsets computed here (li passes through opaque)
       uint16_t* obase = og + (long)(reverse ? (N - tc - n) : tc) * D + col0;
       const int li_c = opaque(li);
-      const int o_lane = 4 * lg + (reverse ? (n - 1 - li_c) : li_c) * D;
+      const int o_lane = 8 * lg + (reverse ? (n - 1 - li_c) : li_c) * D;
       const int o_qb = reverse ? -16 * D : 16 * D;
       // epilogue: gated, weighted rows held until every wave's sums of squares
       // are in LDS
@@ -635,7 +638,7 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               ss = fmaf(acc[ct][r], acc[ct][r], ss);
-              const uint32_t gw = gq[qb][ct][r >> 1];
+              const uint32_t gw = gq[qb][2 * ct + (r >> 1)];
               const float g = (r & 1) ? bf_hi(gw) : bf_lo(gw);
               const float sig = __builtin_amdgcn_rcpf(1.f + fast_exp2(-kLog2e * g));
               z[qb][ct][r] = acc[ct][r] * wn[ct][r] * sig;
@@ -644,11 +647,10 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
           ss = sum_lane_xor32(sum_lane_xor16(ss));
           if (lg == 0) ssq[wave][16 * qb + li] = ss;
         } else if (store) {
-          uint16_t* dst = obase + (o_lane + qb * o_qb);
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct)
-            *reinterpret_cast<u32x2_t*>(dst + 16 * ct) =
-                u32x2_t{pack2(acc[ct][0], acc[ct][1]), pack2(acc[ct][2], acc[ct][3])};
+          // this lane's 8 adjacent columns of row 16qb + li: one 16-byte store
+          *reinterpret_cast<u32x4_t*>(obase + (o_lane + qb * o_qb)) =
+              u32x4_t{pack2(acc[0][0], acc[0][1]), pack2(acc[0][2], acc[0][3]),
+                      pack2(acc[1][0], acc[1][1]), pack2(acc[1][2], acc[1][3])};
         }
       };
       // Full chunk, software-pipelined over query blocks: block qb's Q^T
@@ -755,12 +757,11 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
           for (int w = 0; w < G::NW; ++w) tot += ssq[w][16 * qb + li];
           const float rn = __builtin_amdgcn_rsqf(tot * (1.f / D) + eps);
           if (16 * qb + li_c < n) {
-            uint16_t* dst = obase + (o_lane + qb * o_qb);
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-              *reinterpret_cast<u32x2_t*>(dst + 16 * ct) =
-                  u32x2_t{pack2(z[qb][ct][0] * rn, z[qb][ct][1] * rn),
-                          pack2(z[qb][ct][2] * rn, z[qb][ct][3] * rn)};
+            *reinterpret_cast<u32x4_t*>(obase + (o_lane + qb * o_qb)) =
+                u32x4_t{pack2(z[qb][0][0] * rn, z[qb][0][1] * rn),
+                        pack2(z[qb][0][2] * rn, z[qb][0][3] * rn),
+                        pack2(z[qb][1][0] * rn, z[qb][1][1] * rn),
+                        pack2(z[qb][1][2] * rn, z[qb][1][3] * rn)};
           }
         }
       }
@@ -777,7 +778,7 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          s_final[(size_t)feat(t, r) * D + col0 + 16 * ct + li] = S[t][ct][r];
+          s_final[(size_t)feat(t, r) * D + col0 + vcol(ct, li)] = S[t][ct][r];
   }
 }
 
