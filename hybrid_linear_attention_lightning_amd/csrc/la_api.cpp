@@ -225,6 +225,29 @@ la_status_t run_pass(la_dtype_t dt, const Plan& pl, const la::SeqTable& t, int B
                   t, s);
 }
 
+// The three passes of the backward.  dq_t = S_t dout_t is the causal pass
+// with (q, k, v) -> (dout, v, k).  dk_s = sum_{t>=s} lambda^(t-s) (v_s .
+// dout_t) q_t is the anti-causal pass (v, dout, q) and dv_s = sum_{t>=s}
+// lambda^(t-s) (k_s . q_t) dout_t the anti-causal pass (k, q, dout).  The
+// states of the dv pass (sums of q dout^T) are the transposes of the dk
+// pass's (sums of dout q^T), so the dv pass reads the dk pass's segment
+// start states transposed instead of running its own pre-pass.
+la_status_t run_bwd(la_dtype_t dt, const Plan& pl, const la::SeqTable& t, int B, int H, int N,
+                    int d, int C, const void* q, const void* k, const void* v, const void* dout,
+                    const float* slope, void* dq, void* dk, void* dv, void* workspace,
+                    hipStream_t s) {
+  la_status_t st = run_pass(dt, pl, t, B, H, N, d, C, dout, v, k, slope, nullptr, dq, nullptr,
+                            false, workspace, s);
+  if (st != LA_OK) return st;
+  st = run_pass(dt, pl, t, B, H, N, d, C, v, dout, q, slope, nullptr, dk, nullptr, true,
+                workspace, s);
+  if (st != LA_OK) return st;
+  la::FwdPass fp =
+      make_fwd(pl, B, H, N, d, C, k, q, dout, slope, nullptr, dv, nullptr, true, workspace);
+  fp.seg_states_transposed = true;
+  return run_main(dt, fp, t, s);
+}
+
 // Checks of la_prefill / la_prefill_main (q and o may be null for the prepass).
 la_status_t check_prefill(la_dtype_t dt, int B, int H, int N, int d, int C, const void* q,
                           const void* k, const void* v, const float* slope,
@@ -449,18 +472,8 @@ la_status_t la_prefill_bwd(la_dtype_t dt, int B, int H, int N, int d, int C, con
     const Plan pl = make_plan(dt, B, H, N, d, C);
     if (pl.ws() > 0 && (!workspace || workspace_bytes < pl.ws())) return LA_ERR_WORKSPACE;
     if (pl.ws() > 0 && !aligned16(workspace)) return LA_ERR_ALIGNMENT;
-    const hipStream_t s = (hipStream_t)stream;
-    // dq_t = S_t dout_t: the causal pass with (q, k, v) -> (dout, v, k)
-    st = run_pass(dt, pl, uniform_table(), B, H, N, d, C, dout, v, k, slope, nullptr, dq,
-                  nullptr, false, workspace, s);
-    if (st != LA_OK) return st;
-    // dk_s = sum_{t>=s} lambda^(t-s) (v_s . dout_t) q_t: anti-causal, (v, dout, q)
-    st = run_pass(dt, pl, uniform_table(), B, H, N, d, C, v, dout, q, slope, nullptr, dk,
-                  nullptr, true, workspace, s);
-    if (st != LA_OK) return st;
-    // dv_s = sum_{t>=s} lambda^(t-s) (k_s . q_t) dout_t: anti-causal, (k, q, dout)
-    return run_pass(dt, pl, uniform_table(), B, H, N, d, C, k, q, dout, slope, nullptr, dv,
-                    nullptr, true, workspace, s);
+    return run_bwd(dt, pl, uniform_table(), B, H, N, d, C, q, k, v, dout, slope, dq, dk, dv,
+                   workspace, (hipStream_t)stream);
   } catch (...) {
     return LA_ERR_HIP;
   }
@@ -525,17 +538,9 @@ la_status_t la_prefill_bwd_varlen(la_dtype_t dt, int H, int d, int C, int nseq,
     }
     st = check_workspace(pl, workspace, workspace_bytes);
     if (st != LA_OK) return st;
-    const hipStream_t s = (hipStream_t)stream;
-    const int T = t.T;
     // the three passes of la_prefill_bwd, each sequence reversed in place
-    st = run_pass(dt, pl, t, 1, H, T, d, C, dout, v, k, slope, nullptr, dq, nullptr, false,
-                  workspace, s);
-    if (st != LA_OK) return st;
-    st = run_pass(dt, pl, t, 1, H, T, d, C, v, dout, q, slope, nullptr, dk, nullptr, true,
-                  workspace, s);
-    if (st != LA_OK) return st;
-    return run_pass(dt, pl, t, 1, H, T, d, C, k, q, dout, slope, nullptr, dv, nullptr, true,
-                    workspace, s);
+    return run_bwd(dt, pl, t, 1, H, t.T, d, C, q, k, v, dout, slope, dq, dk, dv, workspace,
+                   (hipStream_t)stream);
   } catch (...) {
     return LA_ERR_HIP;
   }

@@ -116,6 +116,7 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
   const uint16_t *qg = nullptr, *kg, *vg, *gg = nullptr;
   uint16_t* og = nullptr;
   const float* s_init = nullptr;
+  bool s_init_t = false;  // s_init holds S^T
   float* s_final = nullptr;
   if constexpr (STATE_ONLY) {
     // Pieces are numbered by distance from the end of their segment first:
@@ -178,10 +179,12 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
     vg = (const uint16_t*)p.v + head_off;
     og = (uint16_t*)p.o + head_off;
     if constexpr (EPI) gg = (const uint16_t*)p.gate + head_off;
-    if (seg == 0)
+    if (seg == 0) {
       s_init = p.state_in ? p.state_in + (size_t)row.st * D * D : nullptr;
-    else
+    } else {
       s_init = p.seg_states + ((size_t)row.segbase + seg) * D * D;
+      s_init_t = p.seg_states_transposed;
+    }
     if (seg == row.nseg - 1 && p.state_out) s_final = p.state_out + (size_t)row.st * D * D;
   }
   const int N = row.len;  // reversed positions count back from the row's last token
@@ -204,7 +207,9 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        S[t][ct][r] = s_init ? s_init[(size_t)feat(t, r) * D + col0 + vcol(ct, li)] : 0.f;
+        S[t][ct][r] = !s_init ? 0.f
+                      : s_init_t ? s_init[(size_t)(col0 + vcol(ct, li)) * D + feat(t, r)]
+                                 : s_init[(size_t)feat(t, r) * D + col0 + vcol(ct, li)];
 
   // ---- per-lane decay tables --------------------------------------------
   // P^T tile element: key row 16kb + 4lg + r, query column 16qb + li.

@@ -49,6 +49,9 @@ struct FwdPass {
   int nseg;
   int G;
   const float* seg_states;  // [B][H][nseg][D][D] / [H][G][D][D], or nullptr
+  // The segment start states are stored transposed (S^T): a pass whose
+  // states are the transposes of another pass's reuses that pass's pre-pass.
+  bool seg_states_transposed;
   // Output epilogue (forward only), when gate != nullptr:
   // o = RMSNorm_head(o) * norm_w[h] * sigmoid(gate), gate laid out like o.
   const void* gate;
