@@ -225,7 +225,7 @@ la_status_t run_pass(la_dtype_t dt, const Plan& pl, const la::SeqTable& t, int B
                   t, s);
 }
 
-// The three passes of the backward.  dq_t = S_t dout_t is the causal pass
+// The passes of the backward.  dq_t = S_t dout_t is the causal pass
 // with (q, k, v) -> (dout, v, k).  dk_s = sum_{t>=s} lambda^(t-s) (v_s .
 // dout_t) q_t is the anti-causal pass (v, dout, q) and dv_s = sum_{t>=s}
 // lambda^(t-s) (k_s . q_t) dout_t the anti-causal pass (k, q, dout).  The
@@ -239,6 +239,30 @@ la_status_t run_bwd(la_dtype_t dt, const Plan& pl, const la::SeqTable& t, int B,
   la_status_t st = run_pass(dt, pl, t, B, H, N, d, C, dout, v, k, slope, nullptr, dq, nullptr,
                             false, workspace, s);
   if (st != LA_OK) return st;
+  if (dt == LA_BF16 && C <= 64) {
+    // bf16 with chunks of up to 64 tokens: dk and dv in one fused reverse
+    // pass with one state, after the (v, dout, q) pass's segment pre-pass
+    st = run_prepass(pl, t, B, H, N, d, C, dout, q, slope, nullptr, true, workspace, s);
+    if (st != LA_OK) return st;
+    la::BwdPass bp{};
+    bp.q = q;
+    bp.k = k;
+    bp.v = v;
+    bp.dout = dout;
+    bp.dk = dk;
+    bp.dv = dv;
+    bp.slope = slope;
+    bp.B = B;
+    bp.H = H;
+    bp.N = N;
+    bp.D = d;
+    bp.C = C;
+    bp.seg_len = pl.seg_len;
+    bp.nseg = pl.nseg;
+    bp.G = pl.G;
+    if (pl.prepass) bp.seg_states = (const float*)((const char*)workspace + pl.pieces_bytes);
+    return hip_status(la::launch_bwd_kv_bf16(bp, t, s));
+  }
   st = run_pass(dt, pl, t, B, H, N, d, C, v, dout, q, slope, nullptr, dk, nullptr, true,
                 workspace, s);
   if (st != LA_OK) return st;

@@ -49,10 +49,6 @@
 namespace la {
 namespace {
 
-__host__ __device__ constexpr int frag_base(int qb) {
-  // number of 32-key P^T fragments that query blocks 0..qb-1 use (qb/2+1 each)
-  return qb + ((qb & 1) ? (qb >> 1) * (qb >> 1) : (qb >> 1) * ((qb >> 1) - 1));
-}
 
 template <int C, int D, bool STATE_ONLY>
 struct Cfg {
@@ -78,17 +74,6 @@ struct Cfg {
                 "LDS");
 };
 
-// Swizzle of the 16-byte chunk index of row r of a [C][D] bf16 tile.  It
-// depends on r mod 16 only.  In a 64-bank model with 16 lanes served per
-// pass, it keeps the row-fragment reads (16 rows x 16 B), the transposing
-// reads and the 16-byte direct moves free of bank conflicts at D = 128; the
-// K^T read in the state's feature order touches one 8-byte half of each
-// chunk and is 2-way at D = 64.
-template <int D>
-__host__ __device__ constexpr int swz_of(int r) {
-  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  return ((r >> 1) & 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 1) | (((r >> 3) & 1) << 2);
-}
 
 // EPI: the output epilogue (per-head RMSNorm, per-channel weight, sigmoid
 // gate) is applied to the fp32 outputs before they are rounded and stored.

@@ -59,6 +59,22 @@ struct FwdPass {
   float eps;
 };
 
+// The fused reverse pass of the backward (dk and dv together, bf16, C <= 64):
+// token tensors and segment plan as for FwdPass; seg_states holds the segment
+// start states of the (v, dout, q) pass, i.e. sums of dout q^T.
+struct BwdPass {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  void* dk;
+  void* dv;
+  const float* slope;
+  int B, H, N, D, C;
+  int seg_len, nseg, G;
+  const float* seg_states;
+};
+
 // Per-piece local states for the segment pre-pass:
 // piece p of length piece_len ends at token e_p = min(N, (p+1) piece_len) - 1
 // and holds sum_{t in piece} lambda^(e_p - t) k_t v_t^T.
@@ -129,6 +145,7 @@ hipError_t launch_fwd_bf16(const FwdPass& p, const SeqTable& t, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdPass& p, const SeqTable& t, hipStream_t s);
 hipError_t launch_pieces_bf16(const PiecePass& p, const SeqTable& t, hipStream_t s);
 hipError_t launch_scan(const ScanPass& p, const SeqTable& t, hipStream_t s);
+hipError_t launch_bwd_kv_bf16(const BwdPass& p, const SeqTable& t, hipStream_t s);
 hipError_t launch_decode(bool bf16, int B, int H, int D, const void* q, const void* k,
                          const void* v, const float* slope, float* state, void* o,
                          hipStream_t s);
