@@ -239,9 +239,13 @@ la_status_t run_bwd(la_dtype_t dt, const Plan& pl, const la::SeqTable& t, int B,
   la_status_t st = run_pass(dt, pl, t, B, H, N, d, C, dout, v, k, slope, nullptr, dq, nullptr,
                             false, workspace, s);
   if (st != LA_OK) return st;
-  if (dt == LA_BF16 && C <= 64) {
-    // bf16 with chunks of up to 64 tokens: dk and dv in one fused reverse
-    // pass with one state, after the (v, dout, q) pass's segment pre-pass
+  if (dt == LA_BF16) {
+    // bf16: dk and dv in one fused reverse pass with one state, after the
+    // (v, dout, q) pass's segment pre-pass.  The fused pass holds four tiles,
+    // two score sets and the transposed state in LDS, which fits chunks of up
+    // to 64 tokens; with C = 128 it runs 64-token chunks inside the same
+    // segments (segment lengths are multiples of C; the chunk length changes
+    // only the rounding).
     st = run_prepass(pl, t, B, H, N, d, C, dout, q, slope, nullptr, true, workspace, s);
     if (st != LA_OK) return st;
     la::BwdPass bp{};
@@ -256,7 +260,7 @@ la_status_t run_bwd(la_dtype_t dt, const Plan& pl, const la::SeqTable& t, int B,
     bp.H = H;
     bp.N = N;
     bp.D = d;
-    bp.C = C;
+    bp.C = C < 64 ? C : 64;
     bp.seg_len = pl.seg_len;
     bp.nseg = pl.nseg;
     bp.G = pl.G;
