@@ -33,14 +33,15 @@
 //    products carry ~16 significant bits (plain bf16 operands would lose as
 //    much accuracy as the final rounding of the output);
 //  * Q, K and V are staged row-major in LDS with an XOR swizzle of 16-byte
-//    chunks that keeps every access pattern below free of bank conflicts and
-//    depends only on the row modulo 16, so every LDS address is a per-lane
-//    constant plus a compile-time offset; K^T and V^T fragments (contractions
-//    over tokens) come straight from the row-major tiles through the
-//    transposing LDS read of gfx950; Q, K and V move global -> LDS without
-//    passing through registers.
+//    chunks (see swz_of) that depends only on the row modulo 16, so every
+//    LDS address is a per-lane constant plus a compile-time offset; K^T and
+//    V^T fragments (contractions over tokens) come straight from the
+//    row-major tiles through the transposing LDS read of gfx950; Q, K and V
+//    move global -> LDS without passing through registers.
 // The same kernel in STATE_ONLY mode computes piece states (K^T diag(b) V
-// accumulated over a piece) for the segment pre-pass.
+// accumulated over a piece) for the segment pre-pass, and with EPI applies
+// the output epilogue (per-head RMSNorm, weight, sigmoid gate) before the
+// outputs are stored.
 #include <type_traits>
 
 #include "la_common.h"
@@ -48,7 +49,6 @@
 
 namespace la {
 namespace {
-
 
 template <int C, int D, bool STATE_ONLY>
 struct Cfg {
