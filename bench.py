@@ -337,7 +337,7 @@ def bench_decode_tokens(args, torch, la, la_inputs):
         "B": B, "H": H, "d": d, "K": K, "calls": calls,
         "us_per_call": us,
         "tokens_per_s": B * K / (us * 1e-6),
-        "roofline": {"kernel": "fwd_bf16_kernel<32,128> (la_decode_tokens)", "bound": "hbm",
+        "roofline": {"kernel": "decode_kernel<128, bf16, 4> (la_decode_tokens)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "bytes_per_launch": bytes_},
     }
