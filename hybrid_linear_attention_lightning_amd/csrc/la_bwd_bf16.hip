@@ -144,19 +144,22 @@ __global__ __launch_bounds__(D / 32 * 64) void bwd_kv_bf16_kernel(BwdPass p, con
   constexpr int DM_N = C / DM_STEP;
   const int dm_row0 = G::RPI * wave + lane / G::CPR;
   const int dm_col = 8 * ((lane % G::CPR) ^ swz_of<D>(dm_row0 & 15));
-  const int dm_off = (C - 1 - dm_row0) * D + dm_col;
+  const uint32_t dm_off_b = 2u * (uint32_t)((C - 1 - dm_row0) * D + dm_col);
   auto load_direct = [&](const uint16_t* src, uint16_t* tile, int tc, int n) {
     const uint16_t* base = src + (long)(N - tc - n) * D;
     const uint32_t lds0 = opaque_s((uint32_t)(uintptr_t)(tile + G::RPI * wave * D));
     constexpr uint32_t kMoveBytes = 2u * G::RPI * G::NW * D;
+    if (n == C) {
 #pragma unroll
-    for (int m = 0; m < DM_N; ++m) {
-      const int rr = min(dm_row0 + DM_STEP * m, n - 1);
-      const uint32_t off = n == C ? (uint32_t)(dm_off - m * DM_STEP * D)
-                                  : (uint32_t)((n - 1 - rr) * D + dm_col);
-      __builtin_amdgcn_global_load_lds(
-          base + off, (__attribute__((address_space(3))) void*)(uintptr_t)(lds0 + kMoveBytes * m),
-          16, 0, 0);
+      for (int m = 0; m < DM_N; ++m)
+        dma16(buffer_rsrc(base - (long)m * DM_STEP * D), dm_off_b, lds0 + kMoveBytes * m);
+    } else {
+      const auto rs = buffer_rsrc(base);
+#pragma unroll
+      for (int m = 0; m < DM_N; ++m) {
+        const int rr = min(dm_row0 + DM_STEP * m, n - 1);
+        dma16(rs, 2u * (uint32_t)((n - 1 - rr) * D + dm_col), lds0 + kMoveBytes * m);
+      }
     }
   };
 

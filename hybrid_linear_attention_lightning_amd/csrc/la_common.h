@@ -129,6 +129,42 @@ __device__ __forceinline__ uint32_t opaque_s(uint32_t x) {
   asm volatile("" : "+s"(x));
   return x;
 }
+// base + off bytes, for a wave-uniform base and a per-lane unsigned 32-bit
+// byte offset: the operands of the scalar-base + 32-bit vector-offset form
+// of the global memory instructions, which needs no 64-bit vector address
+// arithmetic per access.  The offset passes through an empty asm at each
+// use, so that its widening to 64 bits is not hoisted away from the access
+// (the instruction form is chosen only where the widening is seen).
+__device__ __forceinline__ const uint16_t* at_bytes(const uint16_t* base, uint32_t off) {
+  asm volatile("" : "+v"(off));
+  return reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(base) + off);
+}
+__device__ __forceinline__ uint16_t* at_bytes(uint16_t* base, uint32_t off) {
+  asm volatile("" : "+v"(off));
+  return reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(base) + off);
+}
+// Raw buffer resource (stride 0) over 2 GiB from base: the operand of the
+// buffer memory instructions.  Dword 3 is the gfx9 format word for 32-bit
+// elements.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+                                           0x00020000);
+}
+// Direct move of 16 bytes per lane, from the buffer at byte offset voff
+// (per lane) into LDS: lane i writes the 16 bytes at lds + 16 i.
+//  * The buffer form (buffer_load_dwordx4 ... lds) is used rather than the
+//    global one: the compiler counts a pending global_load_lds among the
+//    LDS-counter events as well, which turns every later LDS wait into a
+//    wait for zero outstanding operations; a buffer load only counts as a
+//    vector-memory operation.
+//  * The loads are marked non-temporal (nt): every byte is read once, and
+//    the streamed tiles need not stay in the caches (measured a few percent
+//    faster on the 128K prefill, main pass and pre-pass).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
+  constexpr int kNonTemporal = 2;  // cache-policy bit nt
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, voff, 0, 0, kNonTemporal);
+}
 // x, known to be the same in every lane, as a scalar value
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

@@ -282,32 +282,29 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
   // instruction as a plain address (through an empty asm), so the compiler
   // does not tie these writes to the tile variables and does not hold later
   // LDS reads of other tiles until they land; the kernel waits for them
-  // itself (vmcnt(0) and a barrier before the tile is read).
+  // itself (a vmcnt wait and a barrier before the tile is read).
   constexpr int DM_STEP = G::RPI * G::NW;  // rows between a lane's moves
   constexpr int DM_N = C / DM_STEP;        // moves per wave and tile
   const int dm_row0 = G::RPI * wave + lane / G::CPR;
   const int dm_col = 8 * ((lane % G::CPR) ^ swz_of<D>(dm_row0 & 15));
-  const int dm_off = (reverse ? (C - 1 - dm_row0) : dm_row0) * D + dm_col;
+  // a full chunk's moves share one per-lane byte offset; move m adds
+  // m * dm_step elements to the (wave-uniform) base
+  const uint32_t dm_off_b = 2u * (uint32_t)((reverse ? (C - 1 - dm_row0) : dm_row0) * D + dm_col);
   const int dm_step = reverse ? -DM_STEP * D : DM_STEP * D;
   auto load_direct = [&](const uint16_t* src, uint16_t* tile, int tc, int n) {
     const uint16_t* base = src + (long)(reverse ? (N - tc - n) : tc) * D;
     const uint32_t lds0 = opaque_s((uint32_t)(uintptr_t)(tile + G::RPI * wave * D));
     constexpr uint32_t kMoveBytes = 2u * G::RPI * G::NW * D;  // LDS bytes between moves
-    // offsets are unsigned 32-bit, so the loads take the scalar-base +
-    // 32-bit vector-offset form
     if (n == C) {
 #pragma unroll
       for (int m = 0; m < DM_N; ++m)
-        __builtin_amdgcn_global_load_lds(
-            base + (uint32_t)(dm_off + m * dm_step),
-            (__attribute__((address_space(3))) void*)(uintptr_t)(lds0 + kMoveBytes * m), 16, 0, 0);
+        dma16(buffer_rsrc(base + (long)m * dm_step), dm_off_b, lds0 + kMoveBytes * m);
     } else {
+      const auto rs = buffer_rsrc(base);
 #pragma unroll
       for (int m = 0; m < DM_N; ++m) {
         const int rr = min(dm_row0 + DM_STEP * m, n - 1);
-        __builtin_amdgcn_global_load_lds(
-            base + (uint32_t)((reverse ? (n - 1 - rr) : rr) * D + dm_col),
-            (__attribute__((address_space(3))) void*)(uintptr_t)(lds0 + kMoveBytes * m), 16, 0, 0);
+        dma16(rs, 2u * (uint32_t)((reverse ? (n - 1 - rr) : rr) * D + dm_col), lds0 + kMoveBytes * m);
       }
     }
   };
@@ -481,9 +478,10 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
           wn[ct][r] = p.norm_w[(size_t)row.h * D + col0 + 8 * lg + 4 * ct + r];
     }
     // All three tiles move straight from HBM to LDS.  Per chunk: K and V
-    // (issued during the previous chunk's outputs) feed the state update,
-    // which gives Q (issued last, once the previous outputs are done with
-    // its tile) time to land before the score tiles need it.
+    // (issued during the previous chunk: V once its tile has been read into
+    // registers, K after the score tiles) feed the state update, which gives
+    // Q (issued last, once the previous outputs are done with its tile) time
+    // to land before the score tiles need it.
     if (tau0 < tau_end) {
       const int n0 = min(C, tau_end - tau0);
       load_direct(kg, Ks, tau0, n0);
@@ -521,22 +519,25 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
       state_update(Ks, vf, n);
 
       // epilogue: this lane's gate values (rows 16qb + li, columns col0 +
-      // 8lg .. +7).  Issued after Q's moves and before the next
-      // chunk's K and V (vector-memory operations complete in order), they
-      // land during the score tiles without delaying either.
+      // 8lg .. +7).  Issued after Q's moves and before the next chunk's V
+      // and K (vector-memory operations complete in order), they land during
+      // the score tiles without delaying either.
       constexpr int kGateLoads = EPI ? G::NQB : 0;
       u32x4_t gq[EPI ? G::NQB : 1];
       if constexpr (EPI) {
-        const uint16_t* gb = gg + (long)tc * D + col0 + 8 * lg;
+        const uint16_t* gb = gg + (long)tc * D + col0;
 #pragma unroll
         for (int qb = 0; qb < G::NQB; ++qb) {
           const int rr = min(16 * qb + li, n - 1);
-          gq[qb] = *reinterpret_cast<const u32x4_t*>(gb + rr * D);
+          gq[qb] = *reinterpret_cast<const u32x4_t*>(at_bytes(gb, 2u * (uint32_t)(rr * D + 8 * lg)));
         }
       }
 
       wait_vmcnt<kGateLoads>();  // Q's moves (issued before the gate loads) are done
-      lds_barrier();  // Q of chunk tc is in LDS
+      lds_barrier();  // Q of chunk tc is in LDS; every wave has read V
+      // V's tile was read into registers at the top of the chunk: the next
+      // chunk's V moves in from here on, a whole chunk ahead of its use
+      if (more) load_direct(vg, Vs, tc + C, n_next);
 
       // ---- masked scores P^T = (K Q^T) * M^T -> LDS as hi/lo B fragments ----
       // Tile (kb, qb), lane (lg, li) holds keys 16kb + 4lg + r of query
@@ -602,18 +603,16 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
         if constexpr (G::NPAIR > 3) if (pr == 3) pair_tiles(std::integral_constant<int, 3>{});
       }
 
-      lds_barrier();  // P^T fragments written; K and V tiles are dead
-      if (more) {
-        load_direct(kg, Ks, tc + C, n_next);
-        load_direct(vg, Vs, tc + C, n_next);
-      }
+      lds_barrier();  // P^T fragments written; the K tile is dead
+      if (more) load_direct(kg, Ks, tc + C, n_next);
 
       // ---- outputs: O^T = diag(a) (S^T Q^T) + V^T P^T, per query block ----
-      // outputs are addressed from the chunk's lowest-address token with
-      // 32-bit offsets computed here (li passes through opaque)
+      // outputs are addressed from the chunk's lowest-address token: a
+      // wave-uniform base per query block and one per-lane byte offset
+      // (li passes through opaque)
       uint16_t* obase = og + (long)(reverse ? (N - tc - n) : tc) * D + col0;
       const int li_c = opaque(li);
-      const int o_lane = 8 * lg + (reverse ? (n - 1 - li_c) : li_c) * D;
+      const uint32_t o_lane_b = 2u * (uint32_t)(8 * lg + (reverse ? (n - 1 - li_c) : li_c) * D);
       const int o_qb = reverse ? -16 * D : 16 * D;
       // epilogue: gated, weighted rows held until every wave's sums of squares
       // are in LDS
@@ -638,7 +637,7 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
           if (lg == 0) ssq[wave][16 * qb + li] = ss;
         } else if (store) {
           // this lane's 8 adjacent columns of row 16qb + li: one 16-byte store
-          *reinterpret_cast<u32x4_t*>(obase + (o_lane + qb * o_qb)) =
+          *reinterpret_cast<u32x4_t*>(at_bytes(obase + qb * o_qb, o_lane_b)) =
               u32x4_t{pack2(acc[0][0], acc[0][1]), pack2(acc[0][2], acc[0][3]),
                       pack2(acc[1][0], acc[1][1]), pack2(acc[1][2], acc[1][3])};
         }
@@ -747,7 +746,7 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
           for (int w = 0; w < G::NW; ++w) tot += ssq[w][16 * qb + li];
           const float rn = __builtin_amdgcn_rsqf(tot * (1.f / D) + eps);
           if (16 * qb + li_c < n) {
-            *reinterpret_cast<u32x4_t*>(obase + (o_lane + qb * o_qb)) =
+            *reinterpret_cast<u32x4_t*>(at_bytes(obase + qb * o_qb, o_lane_b)) =
                 u32x4_t{pack2(z[qb][0][0] * rn, z[qb][0][1] * rn),
                         pack2(z[qb][0][2] * rn, z[qb][0][3] * rn),
                         pack2(z[qb][1][0] * rn, z[qb][1][1] * rn),
