@@ -150,9 +150,11 @@ def test_prefill_then_decode_equals_longer_prefill(oracle_mod):
 
 
 BWD_CASES = [
-    # bf16 with C <= 64 runs the fused dk/dv pass, C = 128 the separate passes
+    # bf16 runs the fused dk/dv pass (with C = 128 in 64-token chunks inside
+    # the 128-token-multiple segments), f32 the separate passes
     ("bf16", 1, 2, 200, 128, 64),
     ("bf16", 2, 2, 333, 64, 128),
+    ("bf16", 1, 2, 300, 128, 128),
     ("bf16", 1, 3, 97, 128, 32),
     ("bf16", 1, 2, 500, 64, 64),
     ("bf16", 2, 3, 300, 64, 32),
