@@ -510,8 +510,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU; --gpus %d (WORLD_SIZE %d) is not "
-              "supported -- sharding is described in DESIGN.md, not built" % (args.gpus, world),
+        print("bench.py: the library runs on one GPU; --gpus %d (WORLD_SIZE %d) is not "
+              "supported: there is no multi-GPU path" % (args.gpus, world),
               file=sys.stderr)
         sys.exit(2)
 

@@ -595,7 +595,7 @@ const char* la_status_string(la_status_t s) {
     case LA_ERR_NULL_POINTER: return "a required pointer is NULL";
     case LA_ERR_BAD_SHAPE: return "bad shape: B, H, N must be >= 1; d or C not supported";
     case LA_ERR_BAD_DTYPE: return "bad dtype: expected LA_F32 or LA_BF16";
-    case LA_ERR_UNSUPPORTED: return "request not supported by this build";
+    case LA_ERR_UNSUPPORTED: return "request not supported by this library version";
     case LA_ERR_WORKSPACE: return "workspace missing or smaller than la_workspace_bytes()";
     case LA_ERR_HIP: return "a HIP launch or runtime call failed";
     case LA_ERR_ALIGNMENT: return "a pointer is not 16-byte aligned";

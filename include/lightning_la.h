@@ -50,7 +50,7 @@ typedef enum {
   LA_ERR_NULL_POINTER = 1, /* a required pointer is NULL                       */
   LA_ERR_BAD_SHAPE = 2,    /* B, H, N < 1, or d / C outside the supported set  */
   LA_ERR_BAD_DTYPE = 3,    /* dtype is not LA_F32 or LA_BF16                   */
-  LA_ERR_UNSUPPORTED = 4,  /* valid request this build does not implement      */
+  LA_ERR_UNSUPPORTED = 4,  /* valid request this version does not implement    */
   LA_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required       */
   LA_ERR_HIP = 6,          /* a HIP launch or runtime call failed              */
   LA_ERR_ALIGNMENT = 7,    /* a pointer is not 16-byte aligned                 */

@@ -5,8 +5,8 @@ none of the method's arithmetic: it only draws random tensors, rounds them to
 the storage precision and lists the per-head slopes that parameterise the decay.
 
 Workload recipe (Ling & Ring 2.6 Technical Report pages, "Hybrid Linear
-Attention" section, give no numbers for the operator; the shapes below are the
-synthetic stand-ins documented in the design doc):
+Attention" section, give no numbers for the operator; the shapes below are
+synthetic stand-ins):
   * q, k, v ~ N(0, 1) / sqrt(d), drawn in fp32, then rounded to bf16
     (round-to-nearest-even) for the bf16 workloads;
   * upstream gradient dO ~ N(0, 1);
