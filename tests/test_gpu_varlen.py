@@ -103,6 +103,8 @@ def test_varlen_prefix_caching_and_in_place_state(oracle_mod):
 BWD_VARLEN_CASES = [
     ("bf16", 2, 128, 64, [0, 1, 64, 64, 200, 1500]),
     ("bf16", 3, 64, 32, [0, 0, 333, 2000]),
+    # C = 128: the fused reverse pass runs 64-token chunks in 128-token-multiple segments
+    ("bf16", 2, 128, 128, [0, 70, 70, 1100, 1300]),
     ("f32", 2, 64, 32, [0, 5, 5, 70, 300]),
 ]
 
