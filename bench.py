@@ -366,8 +366,10 @@ def bench_train(args, torch, la, la_inputs):
         la.prefill(q, k, v, slope, chunk=C, out=o, return_state=False, workspace=ws, stream=stream)
         if e is not None:
             e[1].record(stream)
+        # the backward keeps the forward's workspace and reuses its segment
+        # start states for the dq pass
         la.prefill_bwd(q, k, v, dout, slope, chunk=C, dq=dq, dk=dk, dv=dv, workspace=ws,
-                       stream=stream)
+                       stream=stream, reuse_forward_workspace=True)
         if e is not None:
             e[2].record(stream)
 

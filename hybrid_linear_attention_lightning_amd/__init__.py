@@ -50,6 +50,8 @@ SIGNATURES = {
     "la_decode_step": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "la_decode_tokens": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "la_prefill_bwd": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "la_prefill_bwd_reuse": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
+                                  _P]),
     "la_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "la_prefill_varlen": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "la_prefill_bwd_varlen": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
@@ -257,23 +259,31 @@ def decode_tokens(q, k, v, slope, state, out=None, stream=None):
 
 
 def prefill_bwd(q, k, v, dout, slope, chunk=64, dq=None, dk=None, dv=None,
-                workspace=None, stream=None):
-    """Gradients (dq, dk, dv) of sum(o * dout) for o = prefill(q, k, v, slope)."""
+                workspace=None, stream=None, reuse_forward_workspace=False):
+    """Gradients (dq, dk, dv) of sum(o * dout) for o = prefill(q, k, v, slope).
+
+    With reuse_forward_workspace, workspace must be the one the forward
+    prefill call (same k, v, slope, chunk, no state_in) used, unmodified since:
+    the dq pass then takes the forward's segment start states from it
+    (la_prefill_bwd_reuse)."""
     B, H, N, d = q.shape
     dt = _dtype_code(q)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     nbytes = workspace_bytes(1, dt, B, H, N, d, chunk)
+    if reuse_forward_workspace and nbytes > 0 and workspace is None:
+        raise ValueError("reuse_forward_workspace needs the forward's workspace")
     ws, wsb = _workspace(nbytes, q.device, workspace)
-    code = lib().la_prefill_bwd(
+    fn = "la_prefill_bwd_reuse" if reuse_forward_workspace else "la_prefill_bwd"
+    code = getattr(lib(), fn)(
         dt, B, H, N, d, chunk,
         _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(dout, "dout", q.dtype),
         _dev(slope, "slope", torch.float32), None,
         _dev(dq, "dq", q.dtype), _dev(dk, "dk", q.dtype), _dev(dv, "dv", q.dtype),
         None if ws is None else ws.data_ptr(), wsb, _stream(stream),
     )
-    _check("la_prefill_bwd", code)
+    _check(fn, code)
     return dq, dk, dv
 
 

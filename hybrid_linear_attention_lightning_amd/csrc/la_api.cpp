@@ -232,12 +232,22 @@ la_status_t run_pass(la_dtype_t dt, const Plan& pl, const la::SeqTable& t, int B
 // states of the dv pass (sums of q dout^T) are the transposes of the dk
 // pass's (sums of dout q^T), so the dv pass reads the dk pass's segment
 // start states transposed instead of running its own pre-pass.
+// With fwd_states, the workspace holds the forward's segment start states
+// (sums of k v^T); the dq pass's are their transposes.
 la_status_t run_bwd(la_dtype_t dt, const Plan& pl, const la::SeqTable& t, int B, int H, int N,
                     int d, int C, const void* q, const void* k, const void* v, const void* dout,
                     const float* slope, void* dq, void* dk, void* dv, void* workspace,
-                    hipStream_t s) {
-  la_status_t st = run_pass(dt, pl, t, B, H, N, d, C, dout, v, k, slope, nullptr, dq, nullptr,
-                            false, workspace, s);
+                    hipStream_t s, bool fwd_states = false) {
+  la_status_t st;
+  if (fwd_states) {
+    la::FwdPass fp =
+        make_fwd(pl, B, H, N, d, C, dout, v, k, slope, nullptr, dq, nullptr, false, workspace);
+    fp.seg_states_transposed = true;
+    st = run_main(dt, fp, t, s);
+  } else {
+    st = run_pass(dt, pl, t, B, H, N, d, C, dout, v, k, slope, nullptr, dq, nullptr, false,
+                  workspace, s);
+  }
   if (st != LA_OK) return st;
   if (dt == LA_BF16) {
     // bf16: dk and dv in one fused reverse pass with one state, after the
@@ -324,6 +334,40 @@ la_status_t check_workspace(const Plan& pl, const void* workspace, size_t worksp
   if (pl.ws() > 0 && (!workspace || workspace_bytes < pl.ws())) return LA_ERR_WORKSPACE;
   if (pl.ws() > 0 && !aligned16(workspace)) return LA_ERR_ALIGNMENT;
   return LA_OK;
+}
+
+// la_prefill_bwd, and with fwd_states la_prefill_bwd_reuse (the workspace
+// holds the forward's segment start states; only the bf16 path has them)
+la_status_t prefill_bwd(la_dtype_t dt, int B, int H, int N, int d, int C, const void* q,
+                        const void* k, const void* v, const void* dout, const float* slope,
+                        const float* state_in, void* dq, void* dk, void* dv, void* workspace,
+                        size_t workspace_bytes, void* stream, bool fwd_states) {
+  try {
+    la_status_t st = check_seq(dt, B, H, N, d, C);
+    if (st != LA_OK) return st;
+    if (!q || !k || !v || !dout || !slope || !dq || !dk || !dv) return LA_ERR_NULL_POINTER;
+    if (state_in) return LA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)slope & 3u))
+      return LA_ERR_ALIGNMENT;
+    const size_t esz = dt == LA_BF16 ? 2 : 4;
+    const size_t tb = (size_t)B * H * N * d * esz;
+    const void* ins[4] = {q, k, v, dout};
+    void* outs[3] = {dq, dk, dv};
+    for (int a = 0; a < 3; ++a) {
+      for (int b = 0; b < 4; ++b)
+        if (overlap(outs[a], tb, ins[b], tb)) return LA_ERR_ALIAS;
+      for (int b = a + 1; b < 3; ++b)
+        if (overlap(outs[a], tb, outs[b], tb)) return LA_ERR_ALIAS;
+    }
+    const Plan pl = make_plan(dt, B, H, N, d, C);
+    if (pl.ws() > 0 && (!workspace || workspace_bytes < pl.ws())) return LA_ERR_WORKSPACE;
+    if (pl.ws() > 0 && !aligned16(workspace)) return LA_ERR_ALIGNMENT;
+    return run_bwd(dt, pl, uniform_table(), B, H, N, d, C, q, k, v, dout, slope, dq, dk, dv,
+                   workspace, (hipStream_t)stream, fwd_states && dt == LA_BF16);
+  } catch (...) {
+    return LA_ERR_HIP;
+  }
 }
 
 }  // namespace
@@ -475,36 +519,22 @@ la_status_t la_decode_tokens(la_dtype_t dt, int B, int H, int K, int d, const vo
   }
 }
 
+
 la_status_t la_prefill_bwd(la_dtype_t dt, int B, int H, int N, int d, int C, const void* q,
                            const void* k, const void* v, const void* dout, const float* slope,
                            const float* state_in, void* dq, void* dk, void* dv,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  try {
-    la_status_t st = check_seq(dt, B, H, N, d, C);
-    if (st != LA_OK) return st;
-    if (!q || !k || !v || !dout || !slope || !dq || !dk || !dv) return LA_ERR_NULL_POINTER;
-    if (state_in) return LA_ERR_UNSUPPORTED;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) ||
-        !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)slope & 3u))
-      return LA_ERR_ALIGNMENT;
-    const size_t esz = dt == LA_BF16 ? 2 : 4;
-    const size_t tb = (size_t)B * H * N * d * esz;
-    const void* ins[4] = {q, k, v, dout};
-    void* outs[3] = {dq, dk, dv};
-    for (int a = 0; a < 3; ++a) {
-      for (int b = 0; b < 4; ++b)
-        if (overlap(outs[a], tb, ins[b], tb)) return LA_ERR_ALIAS;
-      for (int b = a + 1; b < 3; ++b)
-        if (overlap(outs[a], tb, outs[b], tb)) return LA_ERR_ALIAS;
-    }
-    const Plan pl = make_plan(dt, B, H, N, d, C);
-    if (pl.ws() > 0 && (!workspace || workspace_bytes < pl.ws())) return LA_ERR_WORKSPACE;
-    if (pl.ws() > 0 && !aligned16(workspace)) return LA_ERR_ALIGNMENT;
-    return run_bwd(dt, pl, uniform_table(), B, H, N, d, C, q, k, v, dout, slope, dq, dk, dv,
-                   workspace, (hipStream_t)stream);
-  } catch (...) {
-    return LA_ERR_HIP;
-  }
+  return prefill_bwd(dt, B, H, N, d, C, q, k, v, dout, slope, state_in, dq, dk, dv, workspace,
+                     workspace_bytes, stream, false);
+}
+
+la_status_t la_prefill_bwd_reuse(la_dtype_t dt, int B, int H, int N, int d, int C, const void* q,
+                                 const void* k, const void* v, const void* dout,
+                                 const float* slope, const float* state_in, void* dq, void* dk,
+                                 void* dv, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return prefill_bwd(dt, B, H, N, d, C, q, k, v, dout, slope, state_in, dq, dk, dv, workspace,
+                     workspace_bytes, stream, true);
 }
 
 la_status_t la_prefill_varlen(la_dtype_t dt, int H, int d, int C, int nseq,

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 2
+#define LA_ABI_VERSION 3
 
 typedef enum {
   LA_OK = 0,
@@ -210,6 +210,29 @@ la_status_t la_prefill_bwd(la_dtype_t dt, int B, int H, int N, int d, int C,
                            const float *state_in, void *dq, void *dk,
                            void *dv, void *workspace, size_t workspace_bytes,
                            void *stream);
+
+/* ------------------------------------------------------------------------ *
+ * la_prefill_bwd_reuse -- la_prefill_bwd for a caller that keeps the forward's
+ * workspace: the dq pass (the causal pass with k and v exchanged, whose states
+ * sum v k^T) takes its segment start states as the transposes of those the
+ * forward left in the workspace (sums of k v^T) instead of computing them
+ * again, which saves its segment pre-pass.
+ *
+ * Arguments and errors as for la_prefill_bwd.  In addition, workspace must be
+ * the workspace of a completed la_prefill (or la_prefill_prepass) call with
+ * the same dt, B, H, N, d, C, k, v and slope and a NULL state_in, unmodified
+ * since (the forward needs as many bytes as the backward).  The library
+ * cannot check this: a workspace that does not hold those states gives wrong
+ * gradients, not an error.  The call overwrites the workspace.  fp32 calls,
+ * and calls whose rows are not split into segments, need no states and give
+ * the same results as la_prefill_bwd.
+ * ------------------------------------------------------------------------ */
+la_status_t la_prefill_bwd_reuse(la_dtype_t dt, int B, int H, int N, int d,
+                                 int C, const void *q, const void *k,
+                                 const void *v, const void *dout,
+                                 const float *slope, const float *state_in,
+                                 void *dq, void *dk, void *dv, void *workspace,
+                                 size_t workspace_bytes, void *stream);
 
 /* Device workspace bytes needed by la_prefill (op = 0) or la_prefill_bwd
  * (op = 1) for these sizes; 0 means NULL may be passed.  Returns (size_t)-1

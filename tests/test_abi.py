@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = la.lib()
-    assert lib.la_abi_version() == 2
+    assert lib.la_abi_version() == 3
     for code in range(9):
         assert lib.la_status_string(code)
     assert lib.la_status_string(123) == b"unknown status"
@@ -80,8 +80,9 @@ def test_decode_validation():
     assert call(o=S_IN + 64) == ALIAS and call(st=Q) == ALIAS
 
 
-def test_backward_validation():
-    f = la.lib().la_prefill_bwd
+@pytest.mark.parametrize("entry", ["la_prefill_bwd", "la_prefill_bwd_reuse"])
+def test_backward_validation(entry):
+    f = getattr(la.lib(), entry)
 
     def call(dt=BF16, N=256, C=64, s_in=None, dq=DQ, dk=DK, dv=DV, ws=None, wsb=0):
         return f(dt, 1, 2, N, 128, C, Q, K, V, DO, SLOPE, s_in, dq, dk, dv, ws, wsb, None)

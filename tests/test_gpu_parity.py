@@ -12,7 +12,7 @@ import torch
 
 import la_inputs
 import hybrid_linear_attention_lightning_amd as la
-from tests._gpu import assert_close, device, to_dev, to_host
+from tests._gpu import assert_close, device, err_ratio, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -176,6 +176,49 @@ def test_backward(oracle_mod, dtype, B, H, N, d, C):
     assert_close(to_host(dq), rq, dtype, "dq")
     assert_close(to_host(dk), rk, dtype, "dk")
     assert_close(to_host(dv), rv, dtype, "dv")
+
+
+REUSE_CASES = [
+    ("bf16", 1, 2, 300, 128, 64),   # segments of one 64-token chunk
+    ("bf16", 2, 2, 333, 64, 128),
+    ("bf16", 1, 3, 500, 128, 32),
+    ("bf16", 16, 16, 70, 128, 64),  # one segment per row: no states to reuse
+    ("f32", 1, 2, 150, 64, 64),
+]
+
+
+@pytest.mark.parametrize("dtype,B,H,N,d,C", REUSE_CASES)
+def test_backward_reusing_forward_workspace(oracle_mod, dtype, B, H, N, d, C):
+    """la_prefill_bwd_reuse after la_prefill on the same workspace: the dq
+    pass takes the forward's segment start states, transposed."""
+    q, k, v = _inputs(500 + N, B, H, N, d, dtype)
+    g = la_inputs.upstream_grad(500 + N, B, H, N, d, dtype=dtype)
+    s = la_inputs.slopes(H)
+    tq, tk, tv, tg = (to_dev(x, dtype) for x in (q, k, v, g))
+    ts = torch.from_numpy(s).to(device())
+    code = la.LA_BF16 if dtype == "bf16" else la.LA_F32
+    ws = torch.empty(max(la.workspace_bytes(0, code, B, H, N, d, C), 16), dtype=torch.uint8,
+                     device=device())
+    la.prefill(tq, tk, tv, ts, chunk=C, workspace=ws)
+    dq, dk, dv = la.prefill_bwd(tq, tk, tv, tg, ts, chunk=C, workspace=ws,
+                                reuse_forward_workspace=True)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle_mod.bwd(q, k, v, g, s)
+    assert_close(to_host(dq), rq, dtype, "dq")
+    assert_close(to_host(dk), rk, dtype, "dk")
+    assert_close(to_host(dv), rv, dtype, "dv")
+    # dk and dv come from the same passes as in la_prefill_bwd
+    dq2, dk2, dv2 = la.prefill_bwd(tq, tk, tv, tg, ts, chunk=C)
+    torch.cuda.synchronize()
+    assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    assert_close(to_host(dq2), rq, dtype, "dq (own pre-pass)")
+    if dtype == "bf16" and la.workspace_bytes(0, code, B, H, N, d, C) > 0:
+        # the states are really read from the workspace: without them dq is wrong
+        ws.zero_()
+        dq3, _, _ = la.prefill_bwd(tq, tk, tv, tg, ts, chunk=C, workspace=ws,
+                                   reuse_forward_workspace=True)
+        torch.cuda.synchronize()
+        assert err_ratio(to_host(dq3), rq, dtype) > 1.0
 
 
 def test_bitwise_deterministic():
