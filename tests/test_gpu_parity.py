@@ -178,6 +178,35 @@ def test_backward(oracle_mod, dtype, B, H, N, d, C):
     assert_close(to_host(dv), rv, dtype, "dv")
 
 
+SPLIT_CASES = [
+    ("bf16", 1, 4, 1000, 128, 128, True),  # several segments per row, with an initial state
+    ("bf16", 2, 2, 300, 64, 64, False),
+    ("f32", 1, 2, 100, 64, 64, True),      # fp32: no segments, no workspace
+]
+
+
+@pytest.mark.parametrize("dtype,B,H,N,d,C,with_state", SPLIT_CASES)
+def test_prefill_in_two_calls_equals_prefill(dtype, B, H, N, d, C, with_state):
+    """la_prefill_prepass then la_prefill_main (the two halves the benchmark
+    times separately) give la_prefill's results bit for bit."""
+    q, k, v = _inputs(600 + N, B, H, N, d, dtype)
+    s = la_inputs.slopes(H)
+    tq, tk, tv = (to_dev(x, dtype) for x in (q, k, v))
+    ts = torch.from_numpy(s).to(device())
+    tS0 = (torch.from_numpy(la_inputs.decode_state(10, B, H, d)).to(device())
+           if with_state else None)
+    o1, S1 = la.prefill(tq, tk, tv, ts, chunk=C, state_in=tS0)
+    code = la.LA_BF16 if dtype == "bf16" else la.LA_F32
+    ws = torch.empty(max(la.workspace_bytes(0, code, B, H, N, d, C), 16), dtype=torch.uint8,
+                     device=device())
+    o2 = torch.empty_like(tq)
+    S2 = torch.empty_like(S1)
+    la.prefill_prepass(tk, tv, ts, C, ws, state_in=tS0)
+    la.prefill_main(tq, tk, tv, ts, C, ws, o2, state_out=S2, state_in=tS0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
 REUSE_CASES = [
     ("bf16", 1, 2, 300, 128, 64),   # segments of one 64-token chunk
     ("bf16", 2, 2, 333, 64, 128),
