@@ -55,6 +55,7 @@ SIGNATURES = {
     "la_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "la_prefill_varlen": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "la_prefill_bwd_varlen": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "la_prefill_bwd_varlen_reuse": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "la_workspace_bytes_varlen": (_Z, [_I, _I, _I, _I, _I, _I, _P]),
     "la_status_string": (ctypes.c_char_p, [_I]),
     "la_abi_version": (_I, []),
@@ -337,9 +338,10 @@ def prefill_varlen(q, k, v, slope, cu_seqlens, chunk=64, state_in=None, out=None
 
 
 def prefill_bwd_varlen(q, k, v, dout, slope, cu_seqlens, chunk=64, dq=None, dk=None, dv=None,
-                       workspace=None, stream=None):
+                       workspace=None, stream=None, reuse_forward_workspace=False):
     """Gradients (dq, dk, dv) [H,T,d] of sum(o * dout) for o = prefill_varlen(...)
-    with zero initial states."""
+    with zero initial states.  reuse_forward_workspace as for prefill_bwd
+    (la_prefill_bwd_varlen_reuse)."""
     H, T, d = q.shape
     dt = _dtype_code(q)
     nseq, cu = _cu_array(cu_seqlens)
@@ -347,15 +349,18 @@ def prefill_bwd_varlen(q, k, v, dout, slope, cu_seqlens, chunk=64, dq=None, dk=N
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     nbytes = workspace_bytes_varlen(1, dt, H, d, chunk, cu_seqlens)
+    if reuse_forward_workspace and nbytes > 0 and workspace is None:
+        raise ValueError("reuse_forward_workspace needs the forward's workspace")
     ws, wsb = _workspace(nbytes, q.device, workspace)
-    code = lib().la_prefill_bwd_varlen(
+    fn = "la_prefill_bwd_varlen_reuse" if reuse_forward_workspace else "la_prefill_bwd_varlen"
+    code = getattr(lib(), fn)(
         dt, H, d, chunk, nseq, cu,
         _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(dout, "dout", q.dtype),
         _dev(slope, "slope", torch.float32),
         _dev(dq, "dq", q.dtype), _dev(dk, "dk", q.dtype), _dev(dv, "dv", q.dtype),
         None if ws is None else ws.data_ptr(), wsb, _stream(stream),
     )
-    _check("la_prefill_bwd_varlen", code)
+    _check(fn, code)
     return dq, dk, dv
 
 

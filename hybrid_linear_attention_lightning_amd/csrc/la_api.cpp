@@ -370,6 +370,41 @@ la_status_t prefill_bwd(la_dtype_t dt, int B, int H, int N, int d, int C, const 
   }
 }
 
+// la_prefill_bwd_varlen, and with fwd_states la_prefill_bwd_varlen_reuse
+la_status_t prefill_bwd_varlen(la_dtype_t dt, int H, int d, int C, int nseq, const int* cu_seqlens,
+                               const void* q, const void* k, const void* v, const void* dout,
+                               const float* slope, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               bool fwd_states) {
+  try {
+    la::SeqTable t;
+    Plan pl;
+    la_status_t st = check_packed(dt, H, d, C, nseq, cu_seqlens, &t, &pl);
+    if (st != LA_OK) return st;
+    if (!q || !k || !v || !dout || !slope || !dq || !dk || !dv) return LA_ERR_NULL_POINTER;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)slope & 3u))
+      return LA_ERR_ALIGNMENT;
+    const size_t esz = dt == LA_BF16 ? 2 : 4;
+    const size_t tb = (size_t)H * t.T * d * esz;
+    const void* ins[4] = {q, k, v, dout};
+    void* outs[3] = {dq, dk, dv};
+    for (int a = 0; a < 3; ++a) {
+      for (int b = 0; b < 4; ++b)
+        if (overlap(outs[a], tb, ins[b], tb)) return LA_ERR_ALIAS;
+      for (int b = a + 1; b < 3; ++b)
+        if (overlap(outs[a], tb, outs[b], tb)) return LA_ERR_ALIAS;
+    }
+    st = check_workspace(pl, workspace, workspace_bytes);
+    if (st != LA_OK) return st;
+    // the three passes of la_prefill_bwd, each sequence reversed in place
+    return run_bwd(dt, pl, t, 1, H, t.T, d, C, q, k, v, dout, slope, dq, dk, dv, workspace,
+                   (hipStream_t)stream, fwd_states && dt == LA_BF16);
+  } catch (...) {
+    return LA_ERR_HIP;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -575,33 +610,17 @@ la_status_t la_prefill_bwd_varlen(la_dtype_t dt, int H, int d, int C, int nseq,
                                   const void* v, const void* dout, const float* slope, void* dq,
                                   void* dk, void* dv, void* workspace, size_t workspace_bytes,
                                   void* stream) {
-  try {
-    la::SeqTable t;
-    Plan pl;
-    la_status_t st = check_packed(dt, H, d, C, nseq, cu_seqlens, &t, &pl);
-    if (st != LA_OK) return st;
-    if (!q || !k || !v || !dout || !slope || !dq || !dk || !dv) return LA_ERR_NULL_POINTER;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) ||
-        !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || ((uintptr_t)slope & 3u))
-      return LA_ERR_ALIGNMENT;
-    const size_t esz = dt == LA_BF16 ? 2 : 4;
-    const size_t tb = (size_t)H * t.T * d * esz;
-    const void* ins[4] = {q, k, v, dout};
-    void* outs[3] = {dq, dk, dv};
-    for (int a = 0; a < 3; ++a) {
-      for (int b = 0; b < 4; ++b)
-        if (overlap(outs[a], tb, ins[b], tb)) return LA_ERR_ALIAS;
-      for (int b = a + 1; b < 3; ++b)
-        if (overlap(outs[a], tb, outs[b], tb)) return LA_ERR_ALIAS;
-    }
-    st = check_workspace(pl, workspace, workspace_bytes);
-    if (st != LA_OK) return st;
-    // the three passes of la_prefill_bwd, each sequence reversed in place
-    return run_bwd(dt, pl, t, 1, H, t.T, d, C, q, k, v, dout, slope, dq, dk, dv, workspace,
-                   (hipStream_t)stream);
-  } catch (...) {
-    return LA_ERR_HIP;
-  }
+  return prefill_bwd_varlen(dt, H, d, C, nseq, cu_seqlens, q, k, v, dout, slope, dq, dk, dv,
+                            workspace, workspace_bytes, stream, false);
+}
+
+la_status_t la_prefill_bwd_varlen_reuse(la_dtype_t dt, int H, int d, int C, int nseq,
+                                        const int* cu_seqlens, const void* q, const void* k,
+                                        const void* v, const void* dout, const float* slope,
+                                        void* dq, void* dk, void* dv, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  return prefill_bwd_varlen(dt, H, d, C, nseq, cu_seqlens, q, k, v, dout, slope, dq, dk, dv,
+                            workspace, workspace_bytes, stream, true);
 }
 
 size_t la_workspace_bytes_varlen(int op, la_dtype_t dt, int H, int d, int C, int nseq,

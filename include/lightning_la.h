@@ -292,6 +292,19 @@ la_status_t la_prefill_bwd_varlen(la_dtype_t dt, int H, int d, int C, int nseq,
                                   void *dq, void *dk, void *dv, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* la_prefill_bwd_varlen_reuse -- la_prefill_bwd_varlen on the workspace of
+ * the matching la_prefill_varlen call, as la_prefill_bwd_reuse is to
+ * la_prefill_bwd: that call must have had the same dt, H, d, C, nseq,
+ * cu_seqlens, k, v and slope and a NULL state_in, and the workspace must be
+ * unmodified since; otherwise the gradients are wrong (not an error). */
+la_status_t la_prefill_bwd_varlen_reuse(la_dtype_t dt, int H, int d, int C,
+                                        int nseq, const int *cu_seqlens,
+                                        const void *q, const void *k,
+                                        const void *v, const void *dout,
+                                        const float *slope, void *dq, void *dk,
+                                        void *dv, void *workspace,
+                                        size_t workspace_bytes, void *stream);
+
 /* Device workspace bytes for la_prefill_varlen (op = 0) or
  * la_prefill_bwd_varlen (op = 1); (size_t)-1 for arguments they would
  * reject. */

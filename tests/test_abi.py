@@ -132,8 +132,9 @@ def test_varlen_validation():
     assert call() == WS and call(ws=WSP, wsb=nws - 1) == WS and call(ws=WSP + 8, wsb=nws) == ALIGN
 
 
-def test_varlen_backward_validation():
-    f = la.lib().la_prefill_bwd_varlen
+@pytest.mark.parametrize("entry", ["la_prefill_bwd_varlen", "la_prefill_bwd_varlen_reuse"])
+def test_varlen_backward_validation(entry):
+    f = getattr(la.lib(), entry)
     cu = (ctypes.c_int * 3)(0, 100, 5000)
 
     def call(dq=DQ, dk=DK, dv=DV, C=64):

@@ -12,7 +12,7 @@ import torch
 
 import la_inputs
 import hybrid_linear_attention_lightning_amd as la
-from tests._gpu import assert_close, device, to_dev, to_host
+from tests._gpu import assert_close, device, err_ratio, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -122,3 +122,39 @@ def test_varlen_backward(oracle_mod, dtype, H, d, C, cu):
     assert_close(to_host(dq), rq, dtype, "dq")
     assert_close(to_host(dk), rk, dtype, "dk")
     assert_close(to_host(dv), rv, dtype, "dv")
+
+
+@pytest.mark.parametrize("dtype,H,d,C,cu", [
+    ("bf16", 2, 128, 64, [0, 1, 64, 64, 200, 1500]),
+    ("bf16", 2, 128, 128, [0, 70, 70, 1100, 1300]),
+    ("f32", 2, 64, 32, [0, 5, 5, 70, 300]),
+])
+def test_varlen_backward_reusing_forward_workspace(oracle_mod, dtype, H, d, C, cu):
+    """la_prefill_bwd_varlen_reuse after la_prefill_varlen (no initial states)
+    on the same workspace."""
+    T = cu[-1]
+    q, k, v = _packed_inputs(900 + T, H, T, d, dtype)
+    g = la_inputs.upstream_grad(900 + T, 1, H, T, d, dtype=dtype)[0]
+    s = la_inputs.slopes(H)
+    tq, tk, tv, tg = (to_dev(x, dtype) for x in (q, k, v, g))
+    ts = torch.from_numpy(s).to(device())
+    code = la.LA_BF16 if dtype == "bf16" else la.LA_F32
+    ws = torch.empty(max(la.workspace_bytes_varlen(0, code, H, d, C, cu), 16),
+                     dtype=torch.uint8, device=device())
+    la.prefill_varlen(tq, tk, tv, ts, cu, chunk=C, workspace=ws)
+    dq, dk, dv = la.prefill_bwd_varlen(tq, tk, tv, tg, ts, cu, chunk=C, workspace=ws,
+                                       reuse_forward_workspace=True)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle_mod.bwd_varlen(q, k, v, g, s, cu)
+    assert_close(to_host(dq), rq, dtype, "dq")
+    assert_close(to_host(dk), rk, dtype, "dk")
+    assert_close(to_host(dv), rv, dtype, "dv")
+    dq2, dk2, dv2 = la.prefill_bwd_varlen(tq, tk, tv, tg, ts, cu, chunk=C)
+    torch.cuda.synchronize()
+    assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    if dtype == "bf16" and la.workspace_bytes_varlen(0, code, H, d, C, cu) > 0:
+        ws.zero_()
+        dq3, _, _ = la.prefill_bwd_varlen(tq, tk, tv, tg, ts, cu, chunk=C, workspace=ws,
+                                          reuse_forward_workspace=True)
+        torch.cuda.synchronize()
+        assert err_ratio(to_host(dq3), rq, dtype) > 1.0
