@@ -285,6 +285,22 @@ def bench_decode(args, torch, la, la_inputs):
     torch.cuda.synchronize()
     copy_gbs = 2 * a.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del a, b
+    # cold steps: the same steps rotate over four copies of the state (537 MB,
+    # twice the 256 MB Infinity Cache), so each step's state was last touched
+    # three steps (805 MB of traffic) earlier and comes from HBM
+    n_rot, cold_steps = 4, min(200, steps)
+    Ss = [S0.clone() for _ in range(n_rot)]
+    for i in range(2 * n_rot):
+        la.decode_step(qs[i], ks[i], vs[i], slope, Ss[i % n_rot], out=o, stream=stream)
+    torch.cuda.synchronize()
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for i in range(cold_steps):
+        la.decode_step(qs[i], ks[i], vs[i], slope, Ss[i % n_rot], out=o, stream=stream)
+    k1.record(stream)
+    torch.cuda.synchronize()
+    cold_us = k0.elapsed_time(k1) * 1e3 / cold_steps
+    del Ss
     res = {
         "B": B, "H": H, "d": d, "steps": steps,
         "us_per_step": us,
@@ -294,6 +310,10 @@ def bench_decode(args, torch, la, la_inputs):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "bytes_per_launch": bytes_},
         "copy_GBs": copy_gbs,
+        "cold": {"us_per_step": cold_us, "steps": cold_steps,
+                 "hbm_frac": bytes_ / (cold_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                 "note": "consecutive steps rotating over 4 state copies (537 MB), so no "
+                         "step finds its state in the Infinity Cache"},
         "note": "the 134 MB state fits the 256 MB Infinity Cache, so repeated steps can "
                 "exceed the HBM rate; copy_GBs is a plain 1 GiB device copy (bytes read + "
                 "written per second) for comparison",
@@ -537,8 +557,9 @@ def main():
     if args.only in (None, "decode"):
         log("decode B=64 ...")
         out["decode"] = bench_decode(args, torch, la, la_inputs)
-        log("  %.2f us/step (graph replay: %s us/step)" % (
-            out["decode"]["us_per_step"], out["decode"]["graph"]["us_per_step"]))
+        log("  %.2f us/step (graph replay: %s us/step; cold, state evicted: %.2f us/step)" % (
+            out["decode"]["us_per_step"], out["decode"]["graph"]["us_per_step"],
+            out["decode"]["cold"]["us_per_step"]))
         log("decode 4 tokens per call, B=64 ...")
         out["decode_tokens"] = bench_decode_tokens(args, torch, la, la_inputs)
         log("  %.2f us/call" % out["decode_tokens"]["us_per_call"])
