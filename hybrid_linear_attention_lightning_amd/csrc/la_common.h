@@ -33,12 +33,6 @@ __host__ __device__ constexpr int swz_of(int r) {
   return ((r >> 1) & 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 1) | (((r >> 3) & 1) << 2);
 }
 
-// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
-__device__ __forceinline__ uint32_t f2bf(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
 // two fp32 -> packed bf16x2 (lo in bits 0..15), round to nearest even; on
 // gfx950 this is one v_cvt_pk_bf16_f32.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -60,20 +54,8 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Position of token / feature x inside its 32-block in the "fragment order"
-// used in LDS: x = 32*blk + 16*h + 4*g + r  ->  32*blk + 8*g + 4*h + r.
-// A lane of group g then reads 8 contiguous elements that are exactly the
-// rows {4g..4g+3} of two consecutive 16-row accumulator tiles, so MFMA
-// results can be fed back as operands without a transpose.
-__device__ __forceinline__ int frag_pos(int x) {
-  return (x & ~31) | (((x >> 2) & 3) << 3) | (((x >> 4) & 1) << 2) | (x & 3);
-}
-
 __device__ __forceinline__ u32x4_t lds_read16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
-}
-__device__ __forceinline__ u32x2_t lds_read8(const uint16_t* p) {
-  return *reinterpret_cast<const u32x2_t*>(p);
 }
 
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
