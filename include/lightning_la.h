@@ -24,7 +24,8 @@
  *   slope                                       : [H] fp32
  *
  * Ownership and threading.  Every pointer argument (except the status
- * strings) is a DEVICE pointer owned by the caller.  The library allocates no
+ * strings and the host array cu_seqlens of the packed-batch calls) is a
+ * DEVICE pointer owned by the caller.  The library allocates no
  * device memory, keeps no pointer after a call returns and holds no mutable
  * global state.  Work is enqueued on `stream` (a hipStream_t passed as void*;
  * NULL is the null stream) and the call returns without synchronising.  Calls
