@@ -6,7 +6,12 @@ tokens/s on the 128K-token workload (B=1, H=32, N=131072, d=128, chunk 128):
 one step is one whole la_prefill call (segment pre-pass + main pass) over the
 sequence, inputs resident in HBM.  The same line carries:
   * "roofline": the main prefill kernel's algorithmic HBM bytes per launch over
-    its HIP-event-timed average duration, against 8 TB/s;
+    its HIP-event-timed average duration, against 8 TB/s ("frac"), and the same
+    bytes over the whole call ("frac_whole_call");
+  * "prefill_8k": the 8K-token prefill (B=1, H=32, N=8192, d=128, chunk 64),
+    timed and reported like the headline;
+  * "tiny_f32": the tiny fp32 prefill (B=1, H=2, N=256, d=64, chunk 64),
+    microseconds per call;
   * "decode": the batched decode step (B=64, H=32, d=128), 1000 consecutive
     steps with fresh q/k/v each, microseconds per step and HBM fraction;
   * "prefill_gated": the same prefill with the fused output epilogue
@@ -18,7 +23,9 @@ sequence, inputs resident in HBM.  The same line carries:
     d=128, chunk 128) continuing from per-sequence states, forward and
     backward;
   * "cpu_baseline": the fp64 CPU oracle on a bounded sample of the headline
-    workload (the first tokens of all 32 heads), on the host's cores.
+    workload (the first tokens of all 32 heads), on the host's cores, with the
+    CPU model, the 8K prefill on all cores and on one core, and samples of the
+    decode and training workloads.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -94,10 +101,13 @@ def prefill_mfma_executed(B, H, N, d, C):
     return chunks * (tiles + pv + inter + state) * 16 * 16 * 32 * 2
 
 
-def bench_prefill(args, torch, la, la_inputs):
-    B, H, N, d, C = 1, 32, 131072, 128, 128
+def bench_prefill(args, torch, la, la_inputs, name="prefill_128k"):
+    """Whole la_prefill calls (segment pre-pass + main pass, timed apart with
+    HIP events on the launch stream) on one of the prefill workloads."""
+    c = la_inputs.CONFIGS[name]
+    B, H, N, d, C = c["B"], c["H"], c["N"], c["d"], c["C"]
     dev = torch.device("cuda:0")
-    q, k, v = la_inputs.qkv_device(2, B, H, N, d, dev, torch.bfloat16)
+    q, k, v = la_inputs.qkv_device(c["seed"], B, H, N, d, dev, torch.bfloat16)
     slope = torch.from_numpy(la_inputs.slopes(H)).to(dev)
     o = torch.empty_like(q)
     S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
@@ -129,7 +139,13 @@ def bench_prefill(args, torch, la, la_inputs):
     pre_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     ms_per_step = total_ms / args.steps
     bytes_, flops = prefill_counts(B, H, N, d, C)
+    executed = prefill_mfma_executed(B, H, N, d, C)
     achieved = bytes_ / (main_ms * 1e-3) / 1e9
+    whole = bytes_ / (ms_per_step * 1e-3) / 1e9
+
+    def tfs(fl, ms):
+        return fl / (ms * 1e-3) / 1e12
+
     res = {
         "B": B, "H": H, "N": N, "d": d, "C": C,
         "ms_per_step": ms_per_step,
@@ -138,28 +154,62 @@ def bench_prefill(args, torch, la, la_inputs):
         "main_kernel_ms": main_ms,
         "prepass_ms": pre_ms,
         "roofline": {
-            "kernel": "fwd_bf16_kernel<128,128> (la_prefill_main)",
+            "kernel": "fwd_bf16_kernel<%d,%d> (la_prefill_main)" % (C, d),
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(),
+            "frac_whole_call": whole / HBM_PEAK_GBS,
+            "achieved_whole_call": whole,
+            "traffic": measured_traffic() if name == "prefill_128k" else None,
             "bytes_per_launch": bytes_,
+            "note": "frac: the main kernel alone (its HIP-event time); frac_whole_call: the "
+                    "same algorithmic bytes over ms_per_step (pre-pass + main pass)",
         },
         "mfma": {
-            "algorithmic_tflops": flops / (main_ms * 1e-3) / 1e12,
-            "algorithmic_frac": flops / (main_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFS,
-            "executed_tflops": prefill_mfma_executed(B, H, N, d, C) / (main_ms * 1e-3) / 1e12,
-            "executed_frac": prefill_mfma_executed(B, H, N, d, C) / (main_ms * 1e-3) / 1e12
-            / BF16_MFMA_PEAK_TFS,
+            "algorithmic_flops": flops,
+            "executed_flops": executed,
+            "algorithmic_frac_main": tfs(flops, main_ms) / BF16_MFMA_PEAK_TFS,
+            "executed_frac_main": tfs(executed, main_ms) / BF16_MFMA_PEAK_TFS,
+            "algorithmic_frac_whole_call": tfs(flops, ms_per_step) / BF16_MFMA_PEAK_TFS,
+            "executed_frac_whole_call": tfs(executed, ms_per_step) / BF16_MFMA_PEAK_TFS,
             "peak_tflops": BF16_MFMA_PEAK_TFS,
+            "note": "executed counts the hi+lo products and dense 16x16 causal tiles the "
+                    "kernel issues (%.2fx the algorithmic flops)" % (executed / flops),
         },
         "workspace_bytes": nws,
     }
     del q, k, v, o, ws
     torch.cuda.empty_cache()
     return res
+
+
+def bench_tiny_f32(args, torch, la, la_inputs):
+    """The tiny fp32 workload (B=1, H=2, N=256, d=64, chunk 64): microseconds
+    per la_prefill call, back to back (launch-latency bound)."""
+    c = la_inputs.CONFIGS["tiny_f32"]
+    B, H, N, d, C = c["B"], c["H"], c["N"], c["d"], c["C"]
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x).to(dev) for x in la_inputs.qkv(c["seed"], B, H, N, d, "f32"))
+    slope = torch.from_numpy(la_inputs.slopes(H)).to(dev)
+    o = torch.empty_like(q)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    calls = 500
+    for _ in range(20):
+        la.prefill(q, k, v, slope, chunk=C, out=o, state_out=S, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(calls):
+        la.prefill(q, k, v, slope, chunk=C, out=o, state_out=S, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    return {"B": B, "H": H, "N": N, "d": d, "C": C, "dtype": "f32", "calls": calls,
+            "us_per_call": us, "tokens_per_s": B * N / (us * 1e-6),
+            "note": "fwd_f32_kernel, one workgroup per head: bound by launch latency"}
 
 
 def bench_prefill_gated(args, torch, la, la_inputs):
@@ -477,10 +527,43 @@ def bench_varlen(args, torch, la, la_inputs):
     return res
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+_ONE_CORE = r"""
+import json, sys, time
+sys.path.insert(0, %r)
+import la_inputs, oracle
+c = la_inputs.CONFIGS["prefill_8k"]
+heads = %d
+q, k, v = la_inputs.qkv(c["seed"], c["B"], heads, c["N"], c["d"], dtype="bf16")
+s = la_inputs.slopes(c["H"])[:heads]
+t0 = time.perf_counter()
+oracle.fwd(q, k, v, s)
+print(json.dumps({"seconds": time.perf_counter() - t0, "threads": oracle.num_threads()}))
+"""
+
+
 def cpu_baseline(args, la_inputs):
-    """The fp64 oracle on the first tokens of the 128K workload (all 32 heads),
-    in pieces of 4096 tokens carried through the state, until about
-    args.cpu_seconds of oracle time have passed."""
+    """The fp64 oracle (test infrastructure, timed as it stands) on bounded
+    samples of the workloads, on the host's cores:
+      * headline: the first tokens of the 128K prefill (all 32 heads), in
+        pieces of 4096 tokens carried through the state, for about
+        args.cpu_seconds;
+      * the 8K prefill: all 32 heads on all cores, and 8 of its 32 heads in
+        a child process with one OpenMP thread (scaled to 32 heads);
+      * decode: a few B=64 H=32 steps; train: forward + backward of the first
+        4096 tokens of every (b, h) row of the training workload."""
+    import subprocess
+
     import oracle
 
     oracle.build()
@@ -494,14 +577,68 @@ def cpu_baseline(args, la_inputs):
         _, S = oracle.fwd(q, k, v, s, S)
         spent += time.perf_counter() - t0
         done += piece
-    return {
+    res = {
         "value": done / spent,
         "unit": "tokens/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": "fp64 recurrent oracle, first %d tokens of the B=1 H=32 d=128 prefill "
                   "(all 32 heads, bf16-valued inputs), %.1f s" % (done, spent),
+        "cpu_model": cpu_model(),
+        "host_logical_cpus": os.cpu_count(),
     }
+    # 8K prefill, all cores
+    c = la_inputs.CONFIGS["prefill_8k"]
+    q, k, v = la_inputs.qkv(c["seed"], c["B"], c["H"], c["N"], c["d"], dtype="bf16")
+    t0 = time.perf_counter()
+    oracle.fwd(q, k, v, la_inputs.slopes(c["H"]))
+    t8 = time.perf_counter() - t0
+    res["prefill_8k"] = {"tokens_per_s": c["B"] * c["N"] / t8, "seconds": t8,
+                         "threads": oracle.num_threads()}
+    # 8K prefill, one core, 8 of the 32 heads (heads are independent)
+    heads = 8
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", _ONE_CORE % (ROOT, heads)], env=env,
+                       capture_output=True, text=True, timeout=300)
+    if r.returncode == 0:
+        one = json.loads(r.stdout.strip().splitlines()[-1])
+        t_full = one["seconds"] * c["H"] / heads
+        res["prefill_8k_1core"] = {"tokens_per_s": c["B"] * c["N"] / t_full,
+                                   "threads": one["threads"],
+                                   "sample": "%d of %d heads in %.2f s, scaled to all heads"
+                                             % (heads, c["H"], one["seconds"])}
+    else:
+        res["prefill_8k_1core"] = {"error": r.stderr[-500:]}
+    del q, k, v
+    # decode: a few steps of the B=64, H=32 state (the oracle copies the state
+    # on each call; the copy is included)
+    c = la_inputs.CONFIGS["decode_b64"]
+    Bd, Hd, dd = c["B"], c["H"], c["d"]
+    sd = la_inputs.slopes(Hd)
+    st = la_inputs.decode_state(c["seed"], Bd, Hd, dd)
+    nsteps = 5
+    t0 = time.perf_counter()
+    for i in range(nsteps):
+        q1, k1, v1 = (x[:, :, 0] for x in la_inputs.qkv(c["seed"], Bd, Hd, 1, dd, "bf16", step=i))
+        _, st = oracle.decode(q1, k1, v1, sd, st)
+    td = (time.perf_counter() - t0) / nsteps
+    res["decode_b64"] = {"us_per_step": td * 1e6, "tokens_per_s": Bd / td, "steps": nsteps}
+    del st
+    # train: forward + backward over the first 4096 tokens of every row
+    c = la_inputs.CONFIGS["train_32k"]
+    n = 4096
+    q, k, v = la_inputs.qkv(c["seed"], c["B"], c["H"], n, c["d"], dtype="bf16")
+    g = la_inputs.upstream_grad(c["seed"], c["B"], c["H"], n, c["d"], dtype="bf16")
+    st_ = la_inputs.slopes(c["H"])
+    t0 = time.perf_counter()
+    oracle.fwd(q, k, v, st_)
+    t_f = time.perf_counter() - t0
+    oracle.bwd(q, k, v, g, st_)
+    t_b = time.perf_counter() - t0 - t_f
+    res["train_32k"] = {"fwd_tokens_per_s": c["B"] * n / t_f, "bwd_tokens_per_s": c["B"] * n / t_b,
+                        "sample": "first %d of %d tokens of all B=%d x H=%d rows"
+                                  % (n, c["N"], c["B"], c["H"])}
+    return res
 
 
 def copy_calibration(torch):
@@ -522,9 +659,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--train-steps", type=int, default=3)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "train", "varlen"], default=None,
+    ap.add_argument("--only", choices=["prefill", "small", "decode", "train", "varlen"],
+                    default=None,
                     help="run one workload only (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB copy (HBM counter calibration)")
@@ -554,6 +692,13 @@ def main():
         log("prefill 128K with the fused output epilogue ...")
         out["prefill_gated"] = bench_prefill_gated(args, torch, la, la_inputs)
         log("  %.3f ms/step" % out["prefill_gated"]["ms_per_step"])
+    if args.only in (None, "small"):
+        log("prefill 8K ...")
+        out["prefill_8k"] = bench_prefill(args, torch, la, la_inputs, "prefill_8k")
+        log("  %.1f us/step" % (out["prefill_8k"]["ms_per_step"] * 1e3))
+        log("tiny fp32 prefill ...")
+        out["tiny_f32"] = bench_tiny_f32(args, torch, la, la_inputs)
+        log("  %.1f us/call" % out["tiny_f32"]["us_per_call"])
     if args.only in (None, "decode"):
         log("decode B=64 ...")
         out["decode"] = bench_decode(args, torch, la, la_inputs)
@@ -596,6 +741,8 @@ def main():
         "roofline": p["roofline"] if p else None,
         "cpu_baseline": cpu,
         "prefill": p,
+        "prefill_8k": out.get("prefill_8k"),
+        "tiny_f32": out.get("tiny_f32"),
         "prefill_gated": out.get("prefill_gated"),
         "decode": out.get("decode"),
         "decode_tokens": out.get("decode_tokens"),

@@ -93,7 +93,9 @@ def _check(fn, code):
         raise LightningError(fn, code, _lib)
 
 
-def _dtype_code(t: torch.Tensor) -> int:
+def _dtype_code(t) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor, got %s" % type(t).__name__)
     if t.dtype == torch.bfloat16:
         return LA_BF16
     if t.dtype == torch.float32:
@@ -101,14 +103,36 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError("expected bfloat16 or float32 tensors, got %s" % t.dtype)
 
 
-def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise TypeError("%s must be a GPU tensor" % name)
-    if not t.is_contiguous():
-        raise ValueError("%s must be contiguous" % name)
-    if dtype is not None and t.dtype != dtype:
-        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
-    return t.data_ptr()
+def _ptrs(device, *specs):
+    """Device addresses of the tensors in `specs`, each (tensor or None, name,
+    shape, dtype), after checking all of them: a torch tensor of exactly that
+    shape and dtype, contiguous, then (in a second round, so that a wrongly
+    sized tensor reports its shape wherever it stands) on the GPU `device`.
+    None stays None.  Every tensor is checked before any launch: the library
+    takes plain pointers and sizes and cannot see a tensor that is too small."""
+    for t, name, shape, dtype in specs:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch tensor, got %s" % (name, type(t).__name__))
+        if tuple(t.shape) != tuple(int(x) for x in shape):
+            raise ValueError("%s must have shape %s, got %s"
+                             % (name, tuple(int(x) for x in shape), tuple(t.shape)))
+        if t.dtype != dtype:
+            raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    out = []
+    for t, name, _, _ in specs:
+        if t is None:
+            out.append(None)
+            continue
+        if not t.is_cuda:
+            raise TypeError("%s must be a GPU tensor" % name)
+        if t.device != device:
+            raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+        out.append(t.data_ptr())
+    return out
 
 
 def _stream(stream) -> int:
@@ -124,12 +148,41 @@ def workspace_bytes(op: int, dtype: int, B: int, H: int, N: int, d: int, C: int)
     return n
 
 
-def _workspace(nbytes: int, device, ws):
+def _workspace(nbytes: int, device, ws, required=False):
+    """(pointer, size) of the workspace: the caller's tensor, checked, or a
+    fresh one when the caller passes none (unless `required`: the call reads
+    states an earlier call left there).  A caller's workspace that is too
+    small is an error, never replaced behind the caller's back."""
     if nbytes == 0:
         return None, 0
-    if ws is None or ws.numel() * ws.element_size() < nbytes:
+    if ws is None:
+        if required:
+            raise ValueError("this call needs the workspace of the earlier call whose "
+                             "segment start states it reads")
         ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
-    return ws, ws.numel() * ws.element_size()
+    if not isinstance(ws, torch.Tensor) or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous torch tensor")
+    size = ws.numel() * ws.element_size()
+    if size < nbytes:
+        raise ValueError("workspace holds %d bytes, %d needed" % (size, nbytes))
+    if not ws.is_cuda or ws.device != device:
+        raise ValueError("workspace must be a GPU tensor on %s" % device)
+    return ws.data_ptr(), size
+
+
+def _same(ref, others):
+    """k, v (and the like) must match q in shape and dtype."""
+    for name, t in others:
+        if not isinstance(t, torch.Tensor) or t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError("%s must match q in shape and dtype" % name)
+
+
+def _shape(t, name, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor, got %s" % (name, type(t).__name__))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dimensions, got shape %s" % (name, ndim, tuple(t.shape)))
+    return tuple(t.shape)
 
 
 def prefill(q, k, v, slope, chunk=64, state_in=None, out=None, state_out=None,
@@ -138,25 +191,21 @@ def prefill(q, k, v, slope, chunk=64, state_in=None, out=None, state_out=None,
 
     Returns (o, state_out) where state_out is [B,H,d,d] fp32 (None when
     return_state is False and no state_out tensor is given)."""
-    B, H, N, d = q.shape
+    B, H, N, d = _shape(q, "q", 4)
     dt = _dtype_code(q)
-    for name, t in (("k", k), ("v", v)):
-        if t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError("%s must match q in shape and dtype" % name)
+    _same(q, (("k", k), ("v", v)))
+    dev = q.device
     if out is None:
         out = torch.empty_like(q)
     if state_out is None and return_state:
-        state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
-    nbytes = workspace_bytes(0, dt, B, H, N, d, chunk)
-    ws, wsb = _workspace(nbytes, q.device, workspace)
-    code = lib().la_prefill(
-        dt, B, H, N, d, chunk,
-        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(slope, "slope", torch.float32),
-        None if state_in is None else _dev(state_in, "state_in", torch.float32),
-        _dev(out, "out", q.dtype),
-        None if state_out is None else _dev(state_out, "state_out", torch.float32),
-        None if ws is None else ws.data_ptr(), wsb, _stream(stream),
-    )
+        state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    sd = (B, H, d, d)
+    args = _ptrs(dev, (q, "q", q.shape, q.dtype), (k, "k", q.shape, q.dtype),
+                 (v, "v", q.shape, q.dtype), (slope, "slope", (H,), torch.float32),
+                 (state_in, "state_in", sd, torch.float32), (out, "out", q.shape, q.dtype),
+                 (state_out, "state_out", sd, torch.float32))
+    ws, wsb = _workspace(workspace_bytes(0, dt, B, H, N, d, chunk), dev, workspace)
+    code = lib().la_prefill(dt, B, H, N, d, chunk, *args, ws, wsb, _stream(stream))
     _check("la_prefill", code)
     return out, state_out
 
@@ -165,28 +214,23 @@ def prefill_gated(q, k, v, slope, gate, norm_weight, eps=1e-6, chunk=64, state_i
                   out=None, state_out=None, return_state=True, workspace=None, stream=None):
     """prefill with the fused output epilogue: y = RMSNorm_head(o) * norm_weight[h]
     * sigmoid(gate), gate like q, norm_weight [H, d] fp32.  Returns (y, state_out)."""
-    B, H, N, d = q.shape
+    B, H, N, d = _shape(q, "q", 4)
     dt = _dtype_code(q)
-    for name, t in (("k", k), ("v", v), ("gate", gate)):
-        if t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError("%s must match q in shape and dtype" % name)
-    if tuple(norm_weight.shape) != (H, d):
-        raise ValueError("norm_weight must be [H, d]")
+    _same(q, (("k", k), ("v", v), ("gate", gate)))
+    dev = q.device
     if out is None:
         out = torch.empty_like(q)
     if state_out is None and return_state:
-        state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
-    nbytes = workspace_bytes(0, dt, B, H, N, d, chunk)
-    ws, wsb = _workspace(nbytes, q.device, workspace)
-    code = lib().la_prefill_gated(
-        dt, B, H, N, d, chunk,
-        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(slope, "slope", torch.float32),
-        None if state_in is None else _dev(state_in, "state_in", torch.float32),
-        _dev(gate, "gate", q.dtype), _dev(norm_weight, "norm_weight", torch.float32), float(eps),
-        _dev(out, "out", q.dtype),
-        None if state_out is None else _dev(state_out, "state_out", torch.float32),
-        None if ws is None else ws.data_ptr(), wsb, _stream(stream),
-    )
+        state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    sd = (B, H, d, d)
+    p = _ptrs(dev, (q, "q", q.shape, q.dtype), (k, "k", q.shape, q.dtype),
+              (v, "v", q.shape, q.dtype), (slope, "slope", (H,), torch.float32),
+              (state_in, "state_in", sd, torch.float32), (gate, "gate", q.shape, q.dtype),
+              (norm_weight, "norm_weight", (H, d), torch.float32), (out, "out", q.shape, q.dtype),
+              (state_out, "state_out", sd, torch.float32))
+    args = p[:7] + [float(eps)] + p[7:]
+    ws, wsb = _workspace(workspace_bytes(0, dt, B, H, N, d, chunk), dev, workspace)
+    code = lib().la_prefill_gated(dt, B, H, N, d, chunk, *args, ws, wsb, _stream(stream))
     _check("la_prefill_gated", code)
     return out, state_out
 
@@ -194,50 +238,53 @@ def prefill_gated(q, k, v, slope, gate, norm_weight, eps=1e-6, chunk=64, state_i
 def prefill_prepass(k, v, slope, chunk, workspace, state_in=None, stream=None):
     """First half of `prefill`: segment start states into `workspace`
     (a uint8 cuda tensor of at least workspace_bytes(0, ...) bytes)."""
-    B, H, N, d = k.shape
+    B, H, N, d = _shape(k, "k", 4)
     dt = _dtype_code(k)
+    dev = k.device
+    args = _ptrs(dev, (k, "k", k.shape, k.dtype), (v, "v", k.shape, k.dtype),
+                 (slope, "slope", (H,), torch.float32),
+                 (state_in, "state_in", (B, H, d, d), torch.float32))
     nbytes = workspace_bytes(0, dt, B, H, N, d, chunk)
-    code = lib().la_prefill_prepass(
-        dt, B, H, N, d, chunk, _dev(k, "k"), _dev(v, "v", k.dtype),
-        _dev(slope, "slope", torch.float32),
-        None if state_in is None else _dev(state_in, "state_in", torch.float32),
-        None if nbytes == 0 else _dev(workspace, "workspace"),
-        0 if nbytes == 0 else workspace.numel() * workspace.element_size(), _stream(stream),
-    )
+    ws, wsb = _workspace(nbytes, dev, workspace, required=True)
+    code = lib().la_prefill_prepass(dt, B, H, N, d, chunk, *args, ws, wsb, _stream(stream))
     _check("la_prefill_prepass", code)
 
 
 def prefill_main(q, k, v, slope, chunk, workspace, out, state_out=None, state_in=None,
                  stream=None):
     """Second half of `prefill`: all segments from the states prefill_prepass
-    left in `workspace`."""
-    B, H, N, d = q.shape
+    left in `workspace` (all-NaN outputs if the workspace does not hold the
+    states of a prepass with the same arguments)."""
+    B, H, N, d = _shape(q, "q", 4)
     dt = _dtype_code(q)
+    _same(q, (("k", k), ("v", v)))
+    dev = q.device
+    sd = (B, H, d, d)
+    if out is None:
+        raise ValueError("prefill_main needs the output tensor")
+    args = _ptrs(dev, (q, "q", q.shape, q.dtype), (k, "k", q.shape, q.dtype),
+                 (v, "v", q.shape, q.dtype), (slope, "slope", (H,), torch.float32),
+                 (state_in, "state_in", sd, torch.float32), (out, "out", q.shape, q.dtype),
+                 (state_out, "state_out", sd, torch.float32))
     nbytes = workspace_bytes(0, dt, B, H, N, d, chunk)
-    code = lib().la_prefill_main(
-        dt, B, H, N, d, chunk, _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
-        _dev(slope, "slope", torch.float32),
-        None if state_in is None else _dev(state_in, "state_in", torch.float32),
-        _dev(out, "out", q.dtype),
-        None if state_out is None else _dev(state_out, "state_out", torch.float32),
-        None if nbytes == 0 else _dev(workspace, "workspace"),
-        0 if nbytes == 0 else workspace.numel() * workspace.element_size(), _stream(stream),
-    )
+    ws, wsb = _workspace(nbytes, dev, workspace, required=True)
+    code = lib().la_prefill_main(dt, B, H, N, d, chunk, *args, ws, wsb, _stream(stream))
     _check("la_prefill_main", code)
     return out
 
 
 def decode_step(q, k, v, slope, state, out=None, stream=None):
     """One decode step.  q, k, v: [B,H,d]; state: [B,H,d,d] fp32 updated in place."""
-    B, H, d = q.shape
+    B, H, d = _shape(q, "q", 3)
     dt = _dtype_code(q)
+    _same(q, (("k", k), ("v", v)))
+    dev = q.device
     if out is None:
         out = torch.empty_like(q)
-    code = lib().la_decode_step(
-        dt, B, H, d, _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
-        _dev(slope, "slope", torch.float32), _dev(state, "state", torch.float32),
-        _dev(out, "out", q.dtype), _stream(stream),
-    )
+    args = _ptrs(dev, (q, "q", q.shape, q.dtype), (k, "k", q.shape, q.dtype),
+                 (v, "v", q.shape, q.dtype), (slope, "slope", (H,), torch.float32),
+                 (state, "state", (B, H, d, d), torch.float32), (out, "out", q.shape, q.dtype))
+    code = lib().la_decode_step(dt, B, H, d, *args, _stream(stream))
     _check("la_decode_step", code)
     return out
 
@@ -246,15 +293,16 @@ def decode_tokens(q, k, v, slope, state, out=None, stream=None):
     """K tokens per (b, h) on a carried state in one call.  q, k, v:
     [B,H,K,d]; state: [B,H,d,d] fp32 updated in place.  Equals K decode_step
     calls."""
-    B, H, K, d = q.shape
+    B, H, K, d = _shape(q, "q", 4)
     dt = _dtype_code(q)
+    _same(q, (("k", k), ("v", v)))
+    dev = q.device
     if out is None:
         out = torch.empty_like(q)
-    code = lib().la_decode_tokens(
-        dt, B, H, K, d, _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
-        _dev(slope, "slope", torch.float32), _dev(state, "state", torch.float32),
-        _dev(out, "out", q.dtype), _stream(stream),
-    )
+    args = _ptrs(dev, (q, "q", q.shape, q.dtype), (k, "k", q.shape, q.dtype),
+                 (v, "v", q.shape, q.dtype), (slope, "slope", (H,), torch.float32),
+                 (state, "state", (B, H, d, d), torch.float32), (out, "out", q.shape, q.dtype))
+    code = lib().la_decode_tokens(dt, B, H, K, d, *args, _stream(stream))
     _check("la_decode_tokens", code)
     return out
 
@@ -266,24 +314,24 @@ def prefill_bwd(q, k, v, dout, slope, chunk=64, dq=None, dk=None, dv=None,
     With reuse_forward_workspace, workspace must be the one the forward
     prefill call (same k, v, slope, chunk, no state_in) used, unmodified since:
     the dq pass then takes the forward's segment start states from it
-    (la_prefill_bwd_reuse)."""
-    B, H, N, d = q.shape
+    (la_prefill_bwd_reuse; dq is all NaN if the workspace holds other
+    states)."""
+    B, H, N, d = _shape(q, "q", 4)
     dt = _dtype_code(q)
+    _same(q, (("k", k), ("v", v), ("dout", dout)))
+    dev = q.device
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
+    p = _ptrs(dev, *((t, n, q.shape, q.dtype) for n, t in (("q", q), ("k", k), ("v", v),
+                                                           ("dout", dout))),
+              (slope, "slope", (H,), torch.float32),
+              *((t, n, q.shape, q.dtype) for n, t in (("dq", dq), ("dk", dk), ("dv", dv))))
+    args = p[:5] + [None] + p[5:]
     nbytes = workspace_bytes(1, dt, B, H, N, d, chunk)
-    if reuse_forward_workspace and nbytes > 0 and workspace is None:
-        raise ValueError("reuse_forward_workspace needs the forward's workspace")
-    ws, wsb = _workspace(nbytes, q.device, workspace)
+    ws, wsb = _workspace(nbytes, dev, workspace, required=reuse_forward_workspace)
     fn = "la_prefill_bwd_reuse" if reuse_forward_workspace else "la_prefill_bwd"
-    code = getattr(lib(), fn)(
-        dt, B, H, N, d, chunk,
-        _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(dout, "dout", q.dtype),
-        _dev(slope, "slope", torch.float32), None,
-        _dev(dq, "dq", q.dtype), _dev(dk, "dk", q.dtype), _dev(dv, "dv", q.dtype),
-        None if ws is None else ws.data_ptr(), wsb, _stream(stream),
-    )
+    code = getattr(lib(), fn)(dt, B, H, N, d, chunk, *args, ws, wsb, _stream(stream))
     _check(fn, code)
     return dq, dk, dv
 
@@ -296,7 +344,16 @@ def _cu_array(cu_seqlens):
             raise TypeError("cu_seqlens must be host data (list, numpy array or CPU tensor)")
         cu_seqlens = cu_seqlens.tolist()
     vals = [int(x) for x in cu_seqlens]
+    if len(vals) < 2:
+        raise ValueError("cu_seqlens needs at least two entries (one sequence)")
     return len(vals) - 1, (ctypes.c_int * len(vals))(*vals)
+
+
+def _packed_T(cu, T, name="q"):
+    """The packed tensors must hold exactly cu_seqlens[-1] tokens: the library
+    takes T = cu_seqlens[nseq] and would address past a shorter tensor."""
+    if cu[len(cu) - 1] != T:
+        raise ValueError("cu_seqlens[-1] = %d but %s holds %d tokens" % (cu[len(cu) - 1], name, T))
 
 
 def workspace_bytes_varlen(op: int, dtype: int, H: int, d: int, C: int, cu_seqlens) -> int:
@@ -310,29 +367,26 @@ def workspace_bytes_varlen(op: int, dtype: int, H: int, d: int, C: int, cu_seqle
 def prefill_varlen(q, k, v, slope, cu_seqlens, chunk=64, state_in=None, out=None,
                    state_out=None, return_state=True, workspace=None, stream=None):
     """Packed batch: q, k, v [H,T,d]; sequence s is tokens
-    cu_seqlens[s] .. cu_seqlens[s+1]-1 (host ints).  Returns (o, state_out)
-    with state_out [nseq,H,d,d] fp32 (None when return_state is False and no
-    state_out tensor is given)."""
-    H, T, d = q.shape
+    cu_seqlens[s] .. cu_seqlens[s+1]-1 (host ints, cu_seqlens[-1] == T).
+    Returns (o, state_out) with state_out [nseq,H,d,d] fp32 (None when
+    return_state is False and no state_out tensor is given)."""
+    H, T, d = _shape(q, "q", 3)
     dt = _dtype_code(q)
-    for name, t in (("k", k), ("v", v)):
-        if t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError("%s must match q in shape and dtype" % name)
+    _same(q, (("k", k), ("v", v)))
     nseq, cu = _cu_array(cu_seqlens)
+    _packed_T(cu, T)
+    dev = q.device
     if out is None:
         out = torch.empty_like(q)
     if state_out is None and return_state:
-        state_out = torch.empty((nseq, H, d, d), dtype=torch.float32, device=q.device)
-    nbytes = workspace_bytes_varlen(0, dt, H, d, chunk, cu_seqlens)
-    ws, wsb = _workspace(nbytes, q.device, workspace)
-    code = lib().la_prefill_varlen(
-        dt, H, d, chunk, nseq, cu,
-        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(slope, "slope", torch.float32),
-        None if state_in is None else _dev(state_in, "state_in", torch.float32),
-        _dev(out, "out", q.dtype),
-        None if state_out is None else _dev(state_out, "state_out", torch.float32),
-        None if ws is None else ws.data_ptr(), wsb, _stream(stream),
-    )
+        state_out = torch.empty((nseq, H, d, d), dtype=torch.float32, device=dev)
+    sd = (nseq, H, d, d)
+    args = _ptrs(dev, (q, "q", q.shape, q.dtype), (k, "k", q.shape, q.dtype),
+                 (v, "v", q.shape, q.dtype), (slope, "slope", (H,), torch.float32),
+                 (state_in, "state_in", sd, torch.float32), (out, "out", q.shape, q.dtype),
+                 (state_out, "state_out", sd, torch.float32))
+    ws, wsb = _workspace(workspace_bytes_varlen(0, dt, H, d, chunk, cu_seqlens), dev, workspace)
+    code = lib().la_prefill_varlen(dt, H, d, chunk, nseq, cu, *args, ws, wsb, _stream(stream))
     _check("la_prefill_varlen", code)
     return out, state_out
 
@@ -342,24 +396,23 @@ def prefill_bwd_varlen(q, k, v, dout, slope, cu_seqlens, chunk=64, dq=None, dk=N
     """Gradients (dq, dk, dv) [H,T,d] of sum(o * dout) for o = prefill_varlen(...)
     with zero initial states.  reuse_forward_workspace as for prefill_bwd
     (la_prefill_bwd_varlen_reuse)."""
-    H, T, d = q.shape
+    H, T, d = _shape(q, "q", 3)
     dt = _dtype_code(q)
+    _same(q, (("k", k), ("v", v), ("dout", dout)))
     nseq, cu = _cu_array(cu_seqlens)
+    _packed_T(cu, T)
+    dev = q.device
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
+    args = _ptrs(dev, *((t, n, q.shape, q.dtype) for n, t in (("q", q), ("k", k), ("v", v),
+                                                              ("dout", dout))),
+                 (slope, "slope", (H,), torch.float32),
+                 *((t, n, q.shape, q.dtype) for n, t in (("dq", dq), ("dk", dk), ("dv", dv))))
     nbytes = workspace_bytes_varlen(1, dt, H, d, chunk, cu_seqlens)
-    if reuse_forward_workspace and nbytes > 0 and workspace is None:
-        raise ValueError("reuse_forward_workspace needs the forward's workspace")
-    ws, wsb = _workspace(nbytes, q.device, workspace)
+    ws, wsb = _workspace(nbytes, dev, workspace, required=reuse_forward_workspace)
     fn = "la_prefill_bwd_varlen_reuse" if reuse_forward_workspace else "la_prefill_bwd_varlen"
-    code = getattr(lib(), fn)(
-        dt, H, d, chunk, nseq, cu,
-        _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype), _dev(dout, "dout", q.dtype),
-        _dev(slope, "slope", torch.float32),
-        _dev(dq, "dq", q.dtype), _dev(dk, "dk", q.dtype), _dev(dv, "dv", q.dtype),
-        None if ws is None else ws.data_ptr(), wsb, _stream(stream),
-    )
+    code = getattr(lib(), fn)(dt, H, d, chunk, nseq, cu, *args, ws, wsb, _stream(stream))
     _check(fn, code)
     return dq, dk, dv
 

@@ -19,13 +19,46 @@ constexpr int kTargetWorkgroups = 256;
 // Upper bound on a piece of the segment pre-pass (tokens).
 constexpr int kMaxPieceLen = 1024;
 
+// Workspace of a segmented plan: piece states, segment start states, then
+// the tag that identifies them (la::WsTag).
 struct Plan {
   int nseg = 1, seg_len = 0, piece_len = 0, npiece = 0;
   int G = 0;             // packed batches: segments per head
   bool prepass = false;  // some row has more than one segment
   size_t pieces_bytes = 0, seg_bytes = 0;
-  size_t ws() const { return pieces_bytes + seg_bytes; }
+  size_t ws() const { return prepass ? pieces_bytes + seg_bytes + la::kTagBytes : 0; }
+  size_t tag_off() const { return pieces_bytes + seg_bytes; }
 };
+
+// The chunk length the kernels run: the bf16 kernels take chunks of 32, 64
+// or 128 tokens, and a bf16 request for 16 runs in 32-token chunks (the chunk
+// length changes only the rounding, never the result).
+int run_chunk(la_dtype_t dt, int C) { return dt == LA_BF16 && C == 16 ? 32 : C; }
+
+// The identity of the segment start states a pre-pass computes: sizes,
+// direction, the k / v / slope / state_in pointers it reads and (packed
+// batches) a hash of the sequence table.
+la::WsTag make_tag(int B, int H, int N, int d, int C, bool reverse, const void* k,
+                   const void* v, const float* slope, const float* state_in,
+                   const la::SeqTable* t) {
+  la::WsTag g{};
+  auto lo = [](const void* x) { return (uint32_t)(uintptr_t)x; };
+  auto hi = [](const void* x) { return (uint32_t)((uint64_t)(uintptr_t)x >> 32); };
+  uint32_t h = 2166136261u;  // FNV-1a over nseq and cu
+  if (t && t->nseq > 0) {
+    auto mix = [&](uint32_t x) {
+      for (int b = 0; b < 4; ++b) h = (h ^ ((x >> (8 * b)) & 0xffu)) * 16777619u;
+    };
+    mix((uint32_t)t->nseq);
+    for (int s = 0; s <= t->nseq; ++s) mix((uint32_t)t->cu[s]);
+  }
+  const uint32_t w[la::kTagWords] = {0x4C415447u, (uint32_t)B, (uint32_t)H, (uint32_t)N,
+                                      (uint32_t)d, (uint32_t)C, reverse ? 1u : 0u, lo(k), hi(k),
+                                      lo(v), hi(v), lo(slope), hi(slope), lo(state_in),
+                                      hi(state_in), h};
+  for (int i = 0; i < la::kTagWords; ++i) g.w[i] = w[i];
+  return g;
+}
 
 // The uniform layout's (empty) sequence table.
 const la::SeqTable& uniform_table() {
@@ -133,7 +166,6 @@ la_status_t hip_status(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_H
 la_status_t check_seq(la_dtype_t dt, int B, int H, int N, int d, int C) {
   if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_BAD_DTYPE;
   if (B < 1 || H < 1 || N < 1 || !d_ok(dt, d) || !c_ok(C)) return LA_ERR_BAD_SHAPE;
-  if (dt == LA_BF16 && C < 32) return LA_ERR_UNSUPPORTED;
   // int indexing of grids and token offsets inside the kernels
   if ((long long)B * H * N > (1LL << 31) / 2) return LA_ERR_UNSUPPORTED;
   return LA_OK;
@@ -162,6 +194,14 @@ la::FwdPass make_fwd(const Plan& pl, int B, int H, int N, int d, int C, const vo
   fp.G = pl.G;
   if (pl.prepass) fp.seg_states = (const float*)((const char*)workspace + pl.pieces_bytes);
   return fp;
+}
+
+// A pass that reads segment start states an earlier call left in the
+// workspace: it checks their tag first.
+void expect_states(la::FwdPass* fp, const Plan& pl, void* workspace, const la::WsTag& tag) {
+  if (!pl.prepass) return;
+  fp->tag = (const uint32_t*)((const char*)workspace + pl.tag_off());
+  fp->tag_expect = tag;
 }
 
 // Segment start states (piece kernel + scan); nothing when there is one segment.
@@ -203,6 +243,8 @@ la_status_t run_prepass(const Plan& pl, const la::SeqTable& t, int B, int H, int
   sp.seg_len = pl.seg_len;
   sp.nseg = pl.nseg;
   sp.G = pl.G;
+  sp.tag = (uint32_t*)((char*)workspace + pl.tag_off());
+  sp.tag_value = make_tag(B, H, N, d, C, reverse, k, v, slope, state_in, &t);
   return hip_status(la::launch_scan(sp, t, s));
 }
 
@@ -243,6 +285,8 @@ la_status_t run_bwd(la_dtype_t dt, const Plan& pl, const la::SeqTable& t, int B,
     la::FwdPass fp =
         make_fwd(pl, B, H, N, d, C, dout, v, k, slope, nullptr, dq, nullptr, false, workspace);
     fp.seg_states_transposed = true;
+    // the forward's states: from (k, v) with no initial state
+    expect_states(&fp, pl, workspace, make_tag(B, H, N, d, C, false, k, v, slope, nullptr, &t));
     st = run_main(dt, fp, t, s);
   } else {
     st = run_pass(dt, pl, t, B, H, N, d, C, dout, v, k, slope, nullptr, dq, nullptr, false,
@@ -319,7 +363,6 @@ la_status_t check_packed(la_dtype_t dt, int H, int d, int C, int nseq, const int
                          la::SeqTable* t, Plan* plan) {
   if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_BAD_DTYPE;
   if (H < 1 || nseq < 1 || !d_ok(dt, d) || !c_ok(C)) return LA_ERR_BAD_SHAPE;
-  if (dt == LA_BF16 && C < 32) return LA_ERR_UNSUPPORTED;
   if (nseq > la::kMaxSeqs) return LA_ERR_UNSUPPORTED;
   if (!cu) return LA_ERR_NULL_POINTER;
   if (cu[0] != 0) return LA_ERR_BAD_SHAPE;
@@ -342,6 +385,7 @@ la_status_t prefill_bwd(la_dtype_t dt, int B, int H, int N, int d, int C, const 
                         const void* k, const void* v, const void* dout, const float* slope,
                         const float* state_in, void* dq, void* dk, void* dv, void* workspace,
                         size_t workspace_bytes, void* stream, bool fwd_states) {
+  C = run_chunk(dt, C);
   try {
     la_status_t st = check_seq(dt, B, H, N, d, C);
     if (st != LA_OK) return st;
@@ -376,6 +420,7 @@ la_status_t prefill_bwd_varlen(la_dtype_t dt, int H, int d, int C, int nseq, con
                                const float* slope, void* dq, void* dk, void* dv,
                                void* workspace, size_t workspace_bytes, void* stream,
                                bool fwd_states) {
+  C = run_chunk(dt, C);
   try {
     la::SeqTable t;
     Plan pl;
@@ -413,6 +458,7 @@ la_status_t la_prefill(la_dtype_t dt, int B, int H, int N, int d, int C, const v
                        const void* k, const void* v, const float* slope, const float* state_in,
                        void* o, float* state_out, void* workspace, size_t workspace_bytes,
                        void* stream) {
+  C = run_chunk(dt, C);
   try {
     Plan pl;
     const la_status_t st = check_prefill(dt, B, H, N, d, C, q, k, v, slope, state_in, o,
@@ -430,6 +476,7 @@ la_status_t la_prefill_gated(la_dtype_t dt, int B, int H, int N, int d, int C, c
                              const float* state_in, const void* gate, const float* norm_weight,
                              float eps, void* y, float* state_out, void* workspace,
                              size_t workspace_bytes, void* stream) {
+  C = run_chunk(dt, C);
   try {
     Plan pl;
     const la_status_t st = check_prefill(dt, B, H, N, d, C, q, k, v, slope, state_in, y,
@@ -462,6 +509,7 @@ la_status_t la_prefill_gated(la_dtype_t dt, int B, int H, int N, int d, int C, c
 la_status_t la_prefill_prepass(la_dtype_t dt, int B, int H, int N, int d, int C, const void* k,
                                const void* v, const float* slope, const float* state_in,
                                void* workspace, size_t workspace_bytes, void* stream) {
+  C = run_chunk(dt, C);
   try {
     Plan pl;
     const la_status_t st = check_prefill(dt, B, H, N, d, C, nullptr, k, v, slope, state_in,
@@ -478,15 +526,18 @@ la_status_t la_prefill_main(la_dtype_t dt, int B, int H, int N, int d, int C, co
                             const void* k, const void* v, const float* slope,
                             const float* state_in, void* o, float* state_out, void* workspace,
                             size_t workspace_bytes, void* stream) {
+  C = run_chunk(dt, C);
   try {
     Plan pl;
     const la_status_t st = check_prefill(dt, B, H, N, d, C, q, k, v, slope, state_in, o,
                                          state_out, workspace, workspace_bytes, true, &pl);
     if (st != LA_OK) return st;
-    return run_main(dt,
-                    make_fwd(pl, B, H, N, d, C, q, k, v, slope, state_in, o, state_out, false,
-                             workspace),
-                    uniform_table(), (hipStream_t)stream);
+    la::FwdPass fp =
+        make_fwd(pl, B, H, N, d, C, q, k, v, slope, state_in, o, state_out, false, workspace);
+    // the states of la_prefill_prepass with the same arguments
+    expect_states(&fp, pl, workspace,
+                  make_tag(B, H, N, d, C, false, k, v, slope, state_in, &uniform_table()));
+    return run_main(dt, fp, uniform_table(), (hipStream_t)stream);
   } catch (...) {
     return LA_ERR_HIP;
   }
@@ -577,6 +628,7 @@ la_status_t la_prefill_varlen(la_dtype_t dt, int H, int d, int C, int nseq,
                               const void* v, const float* slope, const float* state_in, void* o,
                               float* state_out, void* workspace, size_t workspace_bytes,
                               void* stream) {
+  C = run_chunk(dt, C);
   try {
     la::SeqTable t;
     Plan pl;
@@ -625,6 +677,7 @@ la_status_t la_prefill_bwd_varlen_reuse(la_dtype_t dt, int H, int d, int C, int 
 
 size_t la_workspace_bytes_varlen(int op, la_dtype_t dt, int H, int d, int C, int nseq,
                                  const int* cu_seqlens) {
+  C = run_chunk(dt, C);
   if (op != 0 && op != 1) return (size_t)-1;
   la::SeqTable t;
   Plan pl;
@@ -633,6 +686,7 @@ size_t la_workspace_bytes_varlen(int op, la_dtype_t dt, int H, int d, int C, int
 }
 
 size_t la_workspace_bytes(int op, la_dtype_t dt, int B, int H, int N, int d, int C) {
+  C = run_chunk(dt, C);
   if (op != 0 && op != 1) return (size_t)-1;
   if (check_seq(dt, B, H, N, d, C) != LA_OK) return (size_t)-1;
   return make_plan(dt, B, H, N, d, C).ws();

@@ -164,16 +164,27 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
     vg = (const uint16_t*)p.v + head_off;
     og = (uint16_t*)p.o + head_off;
     if constexpr (EPI) gg = (const uint16_t*)p.gate + head_off;
-    if (seg == 0) {
-      s_init = p.state_in ? p.state_in + (size_t)row.st * D * D : nullptr;
-    } else {
+    if (row.nseg > 1) {
+      // segment 0 too: the scan kernel copied state_in into entry 0, so no
+      // workgroup reads state_in while the last segment writes state_out
       s_init = p.seg_states + ((size_t)row.segbase + seg) * D * D;
       s_init_t = p.seg_states_transposed;
+    } else {
+      s_init = p.state_in ? p.state_in + (size_t)row.st * D * D : nullptr;
     }
     if (seg == row.nseg - 1 && p.state_out) s_final = p.state_out + (size_t)row.st * D * D;
   }
   const int N = row.len;  // reversed positions count back from the row's last token
   const float sl2 = slope[row.h] * kLog2e;  // lambda^e = exp2(-sl2 * e)
+  // states from an earlier call: a workspace whose tag is not the expected
+  // one starts the row from NaN, so every output of the pass is NaN
+  bool poison = false;
+  if constexpr (!STATE_ONLY) {
+    if (p.tag) {
+#pragma unroll
+      for (int i = 0; i < kTagWords; ++i) poison |= p.tag[i] != p.tag_expect.w[i];
+    }
+  }
   const int col0 = 32 * wave;                // this wave's first value column
 
   // ---- fp32 state: S[t][ct][r] = S[feature feat(t, r)][value col0 + vcol(ct, li)]
@@ -192,7 +203,8 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        S[t][ct][r] = !s_init ? 0.f
+        S[t][ct][r] = poison    ? __builtin_nanf("")
+                      : !s_init  ? 0.f
                       : s_init_t ? s_init[(size_t)(col0 + vcol(ct, li)) * D + feat(t, r)]
                                  : s_init[(size_t)feat(t, r) * D + col0 + vcol(ct, li)];
 

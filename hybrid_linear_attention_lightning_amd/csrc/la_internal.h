@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace la {
 
@@ -26,6 +27,18 @@ struct SeqTable {
   int ord[kMaxSeqs];
 };
 
+// Identity of the segment start states a pre-pass leaves in a workspace:
+// the sizes, direction and input pointers they were computed from.  The
+// scan kernel writes it behind the states; a pass that reads states computed
+// by an earlier call (la_prefill_main, the _reuse backward) compares it with
+// the identity it expects and, on a mismatch, starts every row from NaN, so
+// that a wrong workspace gives NaN outputs instead of plausible wrong ones.
+constexpr int kTagWords = 16;
+constexpr size_t kTagBytes = 256;  // tag area at the end of the workspace
+struct WsTag {
+  uint32_t w[kTagWords];
+};
+
 // One causal chunked pass o_t = sum_{s<=t} lambda^(t-s) (q_t . k_s) v_s
 // (+ lambda^(t+1) q_t^T S_in) over [B][H][N][D] token tensors.  With
 // reverse = true the pass runs over the time-reversed sequence (token
@@ -42,9 +55,10 @@ struct FwdPass {
   int B, H, N, D, C;
   bool reverse;
   // Segment parallelism: the sequence is cut into nseg segments of seg_len
-  // tokens (a multiple of C); segment r > 0 starts from seg_states[b][h][r]
-  // (entry r = 0 is unused and state_in is used instead).  Packed batches:
-  // G segments per head, seg_states[h][g].
+  // tokens (a multiple of C); when a row has two or more segments, segment r
+  // starts from seg_states[b][h][r], where entry 0 is the scan kernel's copy
+  // of state_in; a row of one segment reads state_in itself.  Packed
+  // batches: G segments per head, seg_states[h][g].
   int seg_len;
   int nseg;
   int G;
@@ -52,6 +66,10 @@ struct FwdPass {
   // The segment start states are stored transposed (S^T): a pass whose
   // states are the transposes of another pass's reuses that pass's pre-pass.
   bool seg_states_transposed;
+  // States from an earlier call: check the workspace tag (tag != nullptr)
+  // against tag_expect before using them.
+  const uint32_t* tag;
+  WsTag tag_expect;
   // Output epilogue (forward only), when gate != nullptr:
   // o = RMSNorm_head(o) * norm_w[h] * sigmoid(gate), gate laid out like o.
   const void* gate;
@@ -90,11 +108,16 @@ struct PiecePass {
   int G;              // packed batches: segments per head
 };
 
-// Segment start states from the piece states (and state_in).
+// Segment start states from the piece states (and state_in).  Entry r = 0 of
+// each row that has two or more segments receives a copy of its state_in (or
+// zeros), so that no workgroup of the main pass reads state_in while another
+// writes state_out (in-place continuation).
 struct ScanPass {
   const float* pieces;     // as PiecePass::pieces
   const float* state_in;   // [B][H][D][D] / [nseq][H][D][D] or nullptr
   float* seg_states;       // as FwdPass::seg_states
+  uint32_t* tag;           // the workspace tag, written by workgroup 0
+  WsTag tag_value;
   const float* slope;
   int B, H, N, D;
   int piece_len, npiece;

@@ -28,6 +28,7 @@ namespace {
 __global__ __launch_bounds__(256) void scan_kernel(ScanPass p, const SeqTable st) {
   // grid: rows x (D*D/4/256 blocks); each thread owns one float4 of the state
   const int D = p.D;
+  if (blockIdx.x == 0 && threadIdx.x < kTagWords) p.tag[threadIdx.x] = p.tag_value.w[threadIdx.x];
   const int per_head = D * D / 4;
   const int r_idx = blockIdx.x / ((per_head + 255) / 256);
   const int e4 = (blockIdx.x % ((per_head + 255) / 256)) * 256 + threadIdx.x;
@@ -49,6 +50,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanPass p, const SeqTable st
   int nneed = 0;
   while (nneed < ppseg && !(sl2 * (float)(nneed * p.piece_len) >= kSkipLog2)) ++nneed;
   const f32x4_t* pc4 = reinterpret_cast<const f32x4_t*>(p.pieces + (size_t)row.piecebase * dd);
+  // entry 0: the row's initial state, read by its first segment
+  reinterpret_cast<f32x4_t*>(p.seg_states + (size_t)row.segbase * dd)[e4] = s;
   for (int r = 1; r < row.nseg; ++r) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) s[c] *= gL;

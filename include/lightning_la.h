@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 3
+#define LA_ABI_VERSION 4
 
 typedef enum {
   LA_OK = 0,
@@ -77,17 +77,24 @@ typedef enum {
  *
  *   dt        LA_F32 or LA_BF16 (type of q, k, v, o)
  *   B, H, N   >= 1;  d in {64, 128} (LA_F32 also allows 16 and 32)
- *   C         chunk length: {16, 32, 64, 128} for LA_F32, {32, 64, 128} for
- *             LA_BF16 (16 gives LA_ERR_UNSUPPORTED); N need not be a multiple
- *             of C.  B*H*N above 2^30 gives LA_ERR_UNSUPPORTED.
+ *   C         chunk length, one of {16, 32, 64, 128}; N need not be a
+ *             multiple of C.  The bf16 kernels run chunks of 32, 64 or 128
+ *             tokens: an LA_BF16 request for C = 16 runs in 32-token chunks,
+ *             which changes only the rounding.  B*H*N above 2^30 gives
+ *             LA_ERR_UNSUPPORTED.
  *   q, k, v   [B][H][N][d] of dt, 16-byte aligned
  *   slope     [H] fp32, the decay is exp(-slope[h]); any finite slope >= 0
  *   state_in  [B][H][d][d] fp32, or NULL for a zero initial state
  *   o         [B][H][N][d] of dt, written; must not overlap q, k or v
  *   state_out [B][H][d][d] fp32 or NULL; may equal state_in (continuation
- *             in place) but must not partially overlap it
+ *             in place) but must not partially overlap it.  In place is
+ *             safe for any plan: when a row is split into segments, the
+ *             pre-pass copies its state_in into the workspace and the first
+ *             segment reads that copy.
  *   workspace device scratch of at least la_workspace_bytes(0, ...) bytes
- *             (may be NULL when that is 0)
+ *             (may be NULL when that is 0).  On return it holds the segment
+ *             start states and a 256-byte tag naming the sizes, direction and
+ *             the k, v, slope and state_in pointers they come from.
  * ------------------------------------------------------------------------ */
 la_status_t la_prefill(la_dtype_t dt, int B, int H, int N, int d, int C,
                        const void *q, const void *k, const void *v,
@@ -137,6 +144,11 @@ la_status_t la_prefill_gated(la_dtype_t dt, int B, int H, int N, int d, int C,
  * reads) and must see the same dt, B, H, N, d, C, k, v, slope, state_in and
  * workspace; the workspace must not be modified between the two calls.  When
  * la_workspace_bytes(0, ...) is 0 the prepass enqueues nothing.
+ * la_prefill_main checks the workspace tag on the device (the library cannot
+ * read device memory without synchronising): if it does not name the same
+ * sizes and k, v, slope and state_in pointers, every output and the final
+ * state are NaN.  The tag names pointers, not contents: states computed from
+ * the same buffers before their contents changed still pass.
  * ------------------------------------------------------------------------ */
 la_status_t la_prefill_prepass(la_dtype_t dt, int B, int H, int N, int d, int C,
                                const void *k, const void *v,
@@ -222,11 +234,14 @@ la_status_t la_prefill_bwd(la_dtype_t dt, int B, int H, int N, int d, int C,
  * Arguments and errors as for la_prefill_bwd.  In addition, workspace must be
  * the workspace of a completed la_prefill (or la_prefill_prepass) call with
  * the same dt, B, H, N, d, C, k, v and slope and a NULL state_in, unmodified
- * since (the forward needs as many bytes as the backward).  The library
- * cannot check this: a workspace that does not hold those states gives wrong
- * gradients, not an error.  The call overwrites the workspace.  fp32 calls,
- * and calls whose rows are not split into segments, need no states and give
- * the same results as la_prefill_bwd.
+ * since (the forward needs as many bytes as the backward).  The dq pass
+ * checks the workspace tag on the device: a workspace whose tag does not name
+ * that forward (same sizes, forward direction, the same k, v and slope
+ * pointers, NULL state_in) gives an all-NaN dq (dk and dv are unaffected);
+ * the status is still LA_OK, since the check runs on the device.  The call
+ * overwrites the workspace and its tag, so a second _reuse call on it gives
+ * NaN.  fp32 calls, and calls whose rows are not split into segments, need no
+ * states and give the same results as la_prefill_bwd.
  * ------------------------------------------------------------------------ */
 la_status_t la_prefill_bwd_reuse(la_dtype_t dt, int B, int H, int N, int d,
                                  int C, const void *q, const void *k,
@@ -236,8 +251,10 @@ la_status_t la_prefill_bwd_reuse(la_dtype_t dt, int B, int H, int N, int d,
                                  size_t workspace_bytes, void *stream);
 
 /* Device workspace bytes needed by la_prefill (op = 0) or la_prefill_bwd
- * (op = 1) for these sizes; 0 means NULL may be passed.  Returns (size_t)-1
- * for arguments the corresponding call would reject. */
+ * (op = 1) for these sizes: the piece and segment start states of the
+ * segment pre-pass plus the 256-byte tag; 0 (no segments) means NULL may be
+ * passed.  Returns (size_t)-1 for arguments the corresponding call would
+ * reject. */
 size_t la_workspace_bytes(int op, la_dtype_t dt, int B, int H, int N, int d,
                           int C);
 
@@ -297,7 +314,8 @@ la_status_t la_prefill_bwd_varlen(la_dtype_t dt, int H, int d, int C, int nseq,
  * the matching la_prefill_varlen call, as la_prefill_bwd_reuse is to
  * la_prefill_bwd: that call must have had the same dt, H, d, C, nseq,
  * cu_seqlens, k, v and slope and a NULL state_in, and the workspace must be
- * unmodified since; otherwise the gradients are wrong (not an error). */
+ * unmodified since; otherwise dq is all NaN (the tag check of
+ * la_prefill_bwd_reuse, with the sequence table hashed into the tag). */
 la_status_t la_prefill_bwd_varlen_reuse(la_dtype_t dt, int H, int d, int C,
                                         int nseq, const int *cu_seqlens,
                                         const void *q, const void *k,

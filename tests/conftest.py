@@ -18,3 +18,17 @@ def oracle_mod():
 
     oracle.build()
     return oracle
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """With LA_MARGINS_OUT set, write the worst parity ratio of every checked
+    tensor (tests._gpu.MARGINS) to that file as JSON."""
+    path = os.environ.get("LA_MARGINS_OUT")
+    if not path:
+        return
+    from tests import _gpu
+    import json
+
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(_gpu.MARGINS, f, indent=1, sort_keys=True)

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = la.lib()
-    assert lib.la_abi_version() == 3
+    assert lib.la_abi_version() == 4
     for code in range(9):
         assert lib.la_status_string(code)
     assert lib.la_status_string(123) == b"unknown status"
@@ -55,7 +55,9 @@ def test_prefill_validation():
     assert prefill(B=0) == SHAPE and prefill(H=0) == SHAPE and prefill(N=0) == SHAPE
     assert prefill(d=96) == SHAPE and prefill(dt=BF16, d=32) == SHAPE
     assert prefill(C=48) == SHAPE and prefill(C=256) == SHAPE
-    assert prefill(dt=BF16, C=16) == UNSUP
+    # bf16 C = 16 is accepted and runs 32-token chunks: same plan, same workspace
+    assert prefill(dt=BF16, C=16) == WS
+    assert la.workspace_bytes(0, BF16, 1, 2, 256, 128, 16) == la.workspace_bytes(0, BF16, 1, 2, 256, 128, 32)
     assert prefill(q=None) == NULLP and prefill(slope=None) == NULLP and prefill(o=None) == NULLP
     assert prefill(q=Q + 8) == ALIGN and prefill(o=O + 2) == ALIGN and prefill(slope=SLOPE + 1) == ALIGN
     assert prefill(s_in=S_IN + 4) == ALIGN
@@ -87,7 +89,7 @@ def test_backward_validation(entry):
     def call(dt=BF16, N=256, C=64, s_in=None, dq=DQ, dk=DK, dv=DV, ws=None, wsb=0):
         return f(dt, 1, 2, N, 128, C, Q, K, V, DO, SLOPE, s_in, dq, dk, dv, ws, wsb, None)
 
-    assert call(C=16) == UNSUP
+    assert call(C=16) == WS
     assert call(dq=None) == NULLP
     assert call(s_in=S_IN) == UNSUP
     assert call(dk=DQ) == ALIAS and call(dv=DO) == ALIAS
@@ -119,7 +121,7 @@ def test_varlen_validation():
     assert call(dt=5) == DTYPE
     assert call(H=0) == SHAPE and call(d=96) == SHAPE and call(C=48) == SHAPE
     assert call(nseq=0) == SHAPE
-    assert call(dt=BF16, C=16) == UNSUP
+    assert call(dt=BF16, C=16) == WS
     assert call(cu=None) == NULLP
     assert call(cu=(1, 100)) == SHAPE  # must start at 0
     assert call(cu=(0, 100, 50)) == SHAPE  # must not decrease
@@ -140,7 +142,7 @@ def test_varlen_backward_validation(entry):
     def call(dq=DQ, dk=DK, dv=DV, C=64):
         return f(BF16, 2, 128, C, 2, cu, Q, K, V, DO, SLOPE, dq, dk, dv, None, 0, None)
 
-    assert call(C=16) == UNSUP and call(dq=None) == NULLP
+    assert call(C=16) == WS and call(dq=None) == NULLP
     assert call(dk=DQ) == ALIAS and call(dv=DO) == ALIAS
     assert call() == WS
 

@@ -12,7 +12,7 @@ import torch
 
 import la_inputs
 import hybrid_linear_attention_lightning_amd as la
-from tests._gpu import assert_close, device, err_ratio, to_dev, to_host
+from tests._gpu import assert_close, device, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -52,6 +52,8 @@ BF16_CASES = [
     (2, 2, 129, 64, 128, False),
     (1, 1, 1000, 64, 32, False),
     (16, 16, 100, 64, 64, False),  # 256 heads: single segment
+    (1, 3, 301, 128, 16, True),    # C = 16 runs 32-token chunks
+    (2, 2, 77, 64, 16, False),
 ]
 
 
@@ -159,6 +161,7 @@ BWD_CASES = [
     ("bf16", 1, 2, 500, 64, 64),
     ("bf16", 2, 3, 300, 64, 32),
     ("bf16", 16, 16, 70, 128, 64),  # 256 heads: one segment, no pre-pass
+    ("bf16", 1, 2, 250, 128, 16),   # C = 16 runs 32-token chunks
     ("f32", 1, 2, 150, 64, 64),
     ("f32", 1, 2, 64, 16, 16),
 ]
@@ -242,12 +245,77 @@ def test_backward_reusing_forward_workspace(oracle_mod, dtype, B, H, N, d, C):
     assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
     assert_close(to_host(dq2), rq, dtype, "dq (own pre-pass)")
     if dtype == "bf16" and la.workspace_bytes(0, code, B, H, N, d, C) > 0:
-        # the states are really read from the workspace: without them dq is wrong
+        # the states are really read from the workspace, and checked: a
+        # workspace without them gives NaN
         ws.zero_()
         dq3, _, _ = la.prefill_bwd(tq, tk, tv, tg, ts, chunk=C, workspace=ws,
                                    reuse_forward_workspace=True)
         torch.cuda.synchronize()
-        assert err_ratio(to_host(dq3), rq, dtype) > 1.0
+        assert torch.isnan(dq3.float()).all()
+
+
+def test_foreign_workspace_gives_nan(oracle_mod):
+    """The workspace tag: a reuse backward, or la_prefill_main, on a
+    workspace that does not hold the states it expects writes NaN outputs;
+    the right workspace gives the oracle's result."""
+    B, H, N, d, C = 1, 2, 300, 128, 64
+    q, k, v = _inputs(520, B, H, N, d, "bf16")
+    g = la_inputs.upstream_grad(520, B, H, N, d, dtype="bf16")
+    s = la_inputs.slopes(H)
+    tq, tk, tv, tg = (to_dev(x, "bf16") for x in (q, k, v, g))
+    ts = torch.from_numpy(s).to(device())
+    nws = la.workspace_bytes(1, la.LA_BF16, B, H, N, d, C)
+    assert nws > 0
+    ws = torch.empty(nws, dtype=torch.uint8, device=device())
+    # forward over a copy of k (same values, another buffer): not this k's states
+    la.prefill(tq, tk.clone(), tv, ts, chunk=C, workspace=ws)
+    dq, dk, dv = la.prefill_bwd(tq, tk, tv, tg, ts, chunk=C, workspace=ws,
+                                reuse_forward_workspace=True)
+    dq0, dk0, dv0 = la.prefill_bwd(tq, tk, tv, tg, ts, chunk=C)
+    torch.cuda.synchronize()
+    assert torch.isnan(dq.float()).all()
+    assert torch.equal(dk, dk0) and torch.equal(dv, dv0)  # dk, dv do not read it
+    # the right forward, then two reuse calls: the first overwrites the states
+    la.prefill(tq, tk, tv, ts, chunk=C, workspace=ws)
+    dq1, _, _ = la.prefill_bwd(tq, tk, tv, tg, ts, chunk=C, workspace=ws,
+                               reuse_forward_workspace=True)
+    dq2, _, _ = la.prefill_bwd(tq, tk, tv, tg, ts, chunk=C, workspace=ws,
+                               reuse_forward_workspace=True)
+    torch.cuda.synchronize()
+    rq, _, _ = oracle_mod.bwd(q, k, v, g, s)
+    assert_close(to_host(dq1), rq, "bf16", "dq")
+    assert torch.isnan(dq2.float()).all()
+    # la_prefill_main after a prepass with another initial state
+    S0 = torch.from_numpy(la_inputs.decode_state(21, B, H, d)).to(device())
+    la.prefill_prepass(tk, tv, ts, C, ws, state_in=S0)
+    o = torch.empty_like(tq)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=device())
+    la.prefill_main(tq, tk, tv, ts, C, ws, o, state_out=S, state_in=None)
+    torch.cuda.synchronize()
+    assert torch.isnan(o.float()).all() and torch.isnan(S).all()
+    la.prefill_main(tq, tk, tv, ts, C, ws, o, state_out=S, state_in=S0)
+    torch.cuda.synchronize()
+    ro, rS = oracle_mod.fwd(q, k, v, s, to_host(S0))
+    assert_close(to_host(o), ro, "bf16", "o")
+    assert_close(to_host(S), rS, "bf16", "S", stored_bf16=False)
+
+
+def test_in_place_continuation_many_segments(oracle_mod):
+    """state_out == state_in on a plan with many segments per row (and more
+    workgroups than compute units): the first segment reads the pre-pass's
+    copy of the initial state, so the last segment's write cannot race it."""
+    B, H, N, d, C = 1, 3, 6000, 64, 32
+    q, k, v = _inputs(521, B, H, N, d, "bf16")
+    s = la_inputs.slopes(H)
+    S0 = la_inputs.decode_state(22, B, H, d)
+    tq, tk, tv = (to_dev(x, "bf16") for x in (q, k, v))
+    tS = torch.from_numpy(S0).to(device())
+    o, _ = la.prefill(tq, tk, tv, torch.from_numpy(s).to(device()), chunk=C, state_in=tS,
+                      state_out=tS)
+    torch.cuda.synchronize()
+    ro, rS = oracle_mod.fwd(q, k, v, s, S0)
+    assert_close(to_host(o), ro, "bf16", "o")
+    assert_close(to_host(tS), rS, "bf16", "S", stored_bf16=False)
 
 
 def test_bitwise_deterministic():
@@ -266,7 +334,7 @@ def test_chunk_length_changes_only_rounding(oracle_mod):
     q, k, v = _inputs(501, B, H, N, d, "bf16")
     s = la_inputs.slopes(H)
     ro, rS = oracle_mod.fwd(q, k, v, s)
-    for C in (32, 64, 128):
+    for C in (16, 32, 64, 128):
         o, S = _run_prefill(q, k, v, s, C, "bf16")
         assert_close(o, ro, "bf16", "o C=%d" % C)
         assert_close(S, rS, "bf16", "S C=%d" % C, stored_bf16=False)
