@@ -43,6 +43,7 @@ STATUS = {
 _P, _I, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 SIGNATURES = {
     "la_prefill": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "la_prefill_noalloc": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "la_prefill_prepass": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
     "la_prefill_gated": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                               _P, _P, _P, _Z, _P]),
@@ -207,6 +208,30 @@ def prefill(q, k, v, slope, chunk=64, state_in=None, out=None, state_out=None,
     ws, wsb = _workspace(workspace_bytes(0, dt, B, H, N, d, chunk), dev, workspace)
     code = lib().la_prefill(dt, B, H, N, d, chunk, *args, ws, wsb, _stream(stream))
     _check("la_prefill", code)
+    return out, state_out
+
+
+def prefill_noalloc(q, k, v, slope, chunk=64, state_in=None, out=None, state_out=None,
+                    return_state=True, stream=None):
+    """`prefill` without a workspace (la_prefill_noalloc): the library's static
+    per-GPU scratch buffer holds the segment states, so the call allocates no
+    device memory when `out` (and `state_out`, or return_state=False) are
+    given.  Calls that overlap on one GPU race."""
+    B, H, N, d = _shape(q, "q", 4)
+    dt = _dtype_code(q)
+    _same(q, (("k", k), ("v", v)))
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    sd = (B, H, d, d)
+    args = _ptrs(dev, (q, "q", q.shape, q.dtype), (k, "k", q.shape, q.dtype),
+                 (v, "v", q.shape, q.dtype), (slope, "slope", (H,), torch.float32),
+                 (state_in, "state_in", sd, torch.float32), (out, "out", q.shape, q.dtype),
+                 (state_out, "state_out", sd, torch.float32))
+    code = lib().la_prefill_noalloc(dt, B, H, N, d, chunk, *args, _stream(stream))
+    _check("la_prefill_noalloc", code)
     return out, state_out
 
 

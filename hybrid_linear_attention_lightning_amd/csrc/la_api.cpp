@@ -7,9 +7,18 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/lightning_la.h"
 #include "la_internal.h"
+
+// The scratch buffer of la_prefill_noalloc: segment start states, piece
+// states and their tag live here instead of in a caller's workspace.  Every
+// GPU the library runs on holds one until the process ends.  In host code
+// the name `scratch` is a host-side stand-in, not a device address: kernels
+// receive the address hipGetSymbolAddress returns for the current device.
+static constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -108,6 +117,24 @@ Plan make_plan(la_dtype_t dt, int B, int H, int N, int d, int C) {
   return p;
 }
 
+// The same segments with fewer, longer pieces, until the workspace fits in
+// cap bytes (the piece length stays a multiple of C dividing the segment
+// length); false if even one piece per segment does not fit.  The piece
+// length changes only the rounding of the segment start states.
+bool fit_plan(Plan* p, long long rows, int d, int C, size_t cap) {
+  if (p->ws() <= cap) return true;
+  const int seg_chunks = p->seg_len / C;
+  const size_t dd = (size_t)d * d * sizeof(float);
+  for (int pc = p->piece_len / C + 1; pc <= seg_chunks; ++pc) {
+    if (seg_chunks % pc) continue;
+    p->piece_len = pc * C;
+    p->npiece = (p->nseg - 1) * (seg_chunks / pc);
+    p->pieces_bytes = (size_t)rows * p->npiece * dd;
+    if (p->ws() <= cap) return true;
+  }
+  return false;
+}
+
 // Packed batch (cu already validated): segments of seg_len tokens, chosen so
 // that the H * sum_s ceil(n_s / seg_len) workgroups fill the GPU; every
 // sequence has at least one segment.  Sequences are scheduled longest first
@@ -161,6 +188,26 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 la_status_t hip_status(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_HIP; }
+
+// Device address of `scratch` on the current device, looked up once per
+// device (each GPU holds its own copy of the array at its own address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+la_status_t scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return LA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return LA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LA_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return LA_OK;
+}
 
 // Shape checks shared by prefill and its backward.
 la_status_t check_seq(la_dtype_t dt, int B, int H, int N, int d, int C) {
@@ -335,7 +382,7 @@ la_status_t check_prefill(la_dtype_t dt, int B, int H, int N, int d, int C, cons
                           const void* k, const void* v, const float* slope,
                           const float* state_in, const void* o, const float* state_out,
                           const void* workspace, size_t workspace_bytes, bool need_qo,
-                          Plan* plan) {
+                          Plan* plan, bool own_workspace = false) {
   la_status_t st = check_seq(dt, B, H, N, d, C);
   if (st != LA_OK) return st;
   if (!k || !v || !slope || (need_qo && (!q || !o))) return LA_ERR_NULL_POINTER;
@@ -353,6 +400,7 @@ la_status_t check_prefill(la_dtype_t dt, int B, int H, int N, int d, int C, cons
                     overlap(state_out, sb, v, tb) || (o && overlap(state_out, sb, o, tb))))
     return LA_ERR_ALIAS;
   *plan = make_plan(dt, B, H, N, d, C);
+  if (own_workspace) return LA_OK;  // the caller of check_prefill provides it
   if (plan->ws() > 0 && (!workspace || workspace_bytes < plan->ws())) return LA_ERR_WORKSPACE;
   if (plan->ws() > 0 && !aligned16(workspace)) return LA_ERR_ALIGNMENT;
   return LA_OK;
@@ -466,6 +514,28 @@ la_status_t la_prefill(la_dtype_t dt, int B, int H, int N, int d, int C, const v
     if (st != LA_OK) return st;
     return run_pass(dt, pl, uniform_table(), B, H, N, d, C, q, k, v, slope, state_in, o,
                     state_out, false, workspace, (hipStream_t)stream);
+  } catch (...) {
+    return LA_ERR_HIP;
+  }
+}
+
+la_status_t la_prefill_noalloc(la_dtype_t dt, int B, int H, int N, int d, int C, const void* q,
+                               const void* k, const void* v, const float* slope,
+                               const float* state_in, void* o, float* state_out, void* stream) {
+  C = run_chunk(dt, C);
+  try {
+    Plan pl;
+    la_status_t st = check_prefill(dt, B, H, N, d, C, q, k, v, slope, state_in, o, state_out,
+                                   nullptr, 0, true, &pl, true);
+    if (st != LA_OK) return st;
+    if (!fit_plan(&pl, (long long)B * H, d, C, kScratchBytes)) return LA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (pl.ws() > 0) {
+      st = scratch_address(&ws);
+      if (st != LA_OK) return st;
+    }
+    return run_pass(dt, pl, uniform_table(), B, H, N, d, C, q, k, v, slope, state_in, o,
+                    state_out, false, ws, (hipStream_t)stream);
   } catch (...) {
     return LA_ERR_HIP;
   }

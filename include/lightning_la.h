@@ -26,8 +26,9 @@
  * Ownership and threading.  Every pointer argument (except the status
  * strings and the host array cu_seqlens of the packed-batch calls) is a
  * DEVICE pointer owned by the caller.  The library allocates no
- * device memory, keeps no pointer after a call returns and holds no mutable
- * global state.  Work is enqueued on `stream` (a hipStream_t passed as void*;
+ * device memory and keeps no pointer after a call returns; its only mutable
+ * global state is the static scratch buffer of la_prefill_noalloc (one per
+ * GPU) and the table of its per-device addresses.  Work is enqueued on `stream` (a hipStream_t passed as void*;
  * NULL is the null stream) and the call returns without synchronising.  Calls
  * on different streams that write the same buffers race.
  *
@@ -101,6 +102,35 @@ la_status_t la_prefill(la_dtype_t dt, int B, int H, int N, int d, int C,
                        const float *slope, const float *state_in, void *o,
                        float *state_out, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ *
+ * la_prefill_noalloc -- la_prefill without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  It allocates nothing:
+ * the segment start states, piece states and their tag go to a static
+ * buffer of the library, 64 MiB per GPU, which each GPU the library runs on
+ * holds until the process ends (its address is looked up once per device,
+ * on the first call with that device current).
+ *
+ *   arguments, results and errors as for la_prefill, without workspace and
+ *   workspace_bytes; the call runs on the current device, and `stream` must
+ *   belong to it.
+ *   When la_prefill's workspace for these sizes would exceed the buffer, the
+ *   same segments are assembled from fewer, longer pieces (this changes only
+ *   the rounding of the segment start states); sizes that still do not fit
+ *   give LA_ERR_WORKSPACE (with d <= 128 at most 48 MiB is needed, so every
+ *   size la_prefill accepts fits).
+ *   Every call on one GPU uses that GPU's one buffer: calls that overlap on
+ *   a GPU (on different streams, or from different threads) race and give
+ *   wrong results; calls on one stream are ordered and safe.  The buffer
+ *   keeps the last call's contents; nothing in it has to start at zero,
+ *   because a call reads only entries it has written itself.
+ * ------------------------------------------------------------------------ */
+la_status_t la_prefill_noalloc(la_dtype_t dt, int B, int H, int N, int d,
+                               int C, const void *q, const void *k,
+                               const void *v, const float *slope,
+                               const float *state_in, void *o,
+                               float *state_out, void *stream);
 
 /* ------------------------------------------------------------------------ *
  * la_prefill_gated -- la_prefill with the layer's output epilogue fused in:

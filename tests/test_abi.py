@@ -191,3 +191,14 @@ def test_gated_prefill_validation():
     assert call(eps=float("inf")) == SHAPE
     assert call(y=G) == ALIAS and call(y=W) == ALIAS
     assert call(ws=None, wsb=0) == WS
+
+
+def test_noalloc_validation():
+    f = la.lib().la_prefill_noalloc
+
+    def call(dt=BF16, B=1, N=256, C=64, q=Q, o=O, s_in=None, s_out=None):
+        return f(dt, B, 2, N, 128, C, q, K, V, SLOPE, s_in, o, s_out, None)
+
+    assert call(dt=7) == DTYPE and call(B=0) == SHAPE and call(C=48) == SHAPE
+    assert call(q=None) == NULLP and call(q=Q + 8) == ALIGN
+    assert call(o=K) == ALIAS and call(s_in=S_IN, s_out=S_IN + 16) == ALIAS
