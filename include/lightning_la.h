@@ -199,9 +199,12 @@ la_status_t la_prefill_main(la_dtype_t dt, int B, int H, int N, int d, int C,
  * operation used for decoding ("Hybrid Linear Attention" section: O(n)
  * training and decoding).
  *
+ *   B, H      >= 1, B*H at most 2^30 (LA_ERR_UNSUPPORTED above)
  *   q, k, v   [B][H][d] of dt
  *   slope     [H] fp32
- *   state     [B][H][d][d] fp32, read and written in place
+ *   state     [B][H][d][d] fp32, read and written in place with
+ *             non-temporal accesses (streamed from and to HBM, not kept in
+ *             the caches)
  *   o         [B][H][d] of dt, written; must not overlap q, k, v or state
  * ------------------------------------------------------------------------ */
 la_status_t la_decode_step(la_dtype_t dt, int B, int H, int d, const void *q,
