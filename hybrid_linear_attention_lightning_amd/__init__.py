@@ -116,13 +116,13 @@ def _ptrs(device, *specs):
             continue
         if not isinstance(t, torch.Tensor):
             raise TypeError("%s must be a torch tensor, got %s" % (name, type(t).__name__))
-        if tuple(t.shape) != tuple(int(x) for x in shape):
-            raise ValueError("%s must have shape %s, got %s"
-                             % (name, tuple(int(x) for x in shape), tuple(t.shape)))
-        if t.dtype != dtype:
+        if t.shape != shape:
+            raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+        if t.dtype is not dtype:
             raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
         if not t.is_contiguous():
             raise ValueError("%s must be contiguous" % name)
+    index = device.index
     out = []
     for t, name, _, _ in specs:
         if t is None:
@@ -130,7 +130,7 @@ def _ptrs(device, *specs):
             continue
         if not t.is_cuda:
             raise TypeError("%s must be a GPU tensor" % name)
-        if t.device != device:
+        if t.get_device() != index:
             raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
         out.append(t.data_ptr())
     return out

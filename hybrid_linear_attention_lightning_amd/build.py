@@ -4,7 +4,9 @@
 
 Compiles every source under csrc/ with hipcc for --offload-arch=gfx950 and
 links one shared library with the C ABI declared in include/lightning_la.h.
-hipcc cross-compiles, so no GPU is needed to build.
+hipcc cross-compiles, so no GPU is needed to build.  LA_EXTRA_FLAGS (an
+environment variable) appends hipcc flags, e.g. to build a copy with other
+definitions for comparison.
 """
 from __future__ import annotations
 
@@ -35,7 +37,7 @@ FLAGS = [
     # AGPRs cost a copy in and out for each such access (measured ~4% faster)
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE,
-]
+] + os.environ.get("LA_EXTRA_FLAGS", "").split()
 
 
 def sources():

@@ -180,9 +180,9 @@ hipError_t launch_decode_tokens(bool bf16, int B, int H, int K, int D, const voi
 
 // Decay factors below this power of two are treated as exact zeros when a
 // segment start state is assembled from piece states: lambda^dist < 2^-kSkipLog2
-// means the piece contributes less than 2^-64 of its own magnitude, 2^40 below
-// the fp32 resolution of a sum that also holds the undecayed last piece of
-// the segment (pieces have equal lengths).
-constexpr float kSkipLog2 = 64.0f;
+// means the piece contributes less than 2^-32 of its own magnitude, 2^8 below
+// the fp32 resolution (2^-24) of a sum that also holds the undecayed last
+// piece of the segment (pieces have equal lengths).
+constexpr float kSkipLog2 = 32.0f;
 
 }  // namespace la

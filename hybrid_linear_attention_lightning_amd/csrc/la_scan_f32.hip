@@ -74,20 +74,39 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanPass p, const SeqTable st
   }
 }
 
-// EPI: the output epilogue (per-head RMSNorm, per-channel weight, sigmoid
-// gate) on each block's fp32 output rows, staged in LDS, before the store.
-template <int D, int CS, bool EPI>
+// fp32 forward, one workgroup per (row, slice of W value columns): the
+// outputs and state of a column depend on all keys but only on that column of
+// V, so the columns split across workgroups with no exchange; the masked
+// scores of a block are recomputed by each slice (W = D for the epilogue,
+// whose norm needs whole rows).  Per block of CS <= C rows:
+//   P = (Q K^T) * M                        (CS x CS, 4 x 4 / 2 x 2 / 1 x 1 register tiles)
+//   O[:, cols] = P V[:, cols] + diag(a) Q S[:, cols]
+//   S[:, cols] = lambda^n S[:, cols] + K^T diag(b) V[:, cols]
+// Each thread keeps its rows x 4 columns of the state slice in registers; a
+// copy in LDS serves the block's inter-block products.  All LDS reads are
+// 16-byte vectors along the contraction (rows padded by 4 floats).
+template <int D, int CS, int W, bool EPI>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdPass p, const SeqTable st) {
-  constexpr int DS = D + 1;  // padded row stride
-  __shared__ float Sm[D * D];
-  __shared__ float Qm[CS * DS], Km[CS * DS], Vm[CS * DS];
-  __shared__ float Pm[CS * (CS + 1)];
+  static_assert(CS == 16 || CS == 32 || CS == 64, "block rows");
+  constexpr int DP = D + 4;             // padded row of Q and K
+  constexpr int WP = W + 4;             // padded row of V and of the state slice
+  constexpr int CP = CS + 4;            // padded row of P
+  constexpr int TC = W / 4;             // float4 column groups of the slice
+  constexpr int RG = 256 / TC;          // row groups (outputs and state)
+  constexpr int OR = CS / RG > 0 ? CS / RG : 1;  // output rows per thread
+  constexpr int SR = D / RG > 0 ? D / RG : 1;    // state rows per thread
+  constexpr int PB = CS / 16;           // score tile per thread: PB x PB
+  static_assert(RG * OR >= CS || RG >= CS, "output rows");
+  __shared__ __attribute__((aligned(16))) float Qm[CS * DP], Km[CS * DP], Vm[CS * WP];
+  __shared__ __attribute__((aligned(16))) float Pm[CS * CP], Sm[D * WP];
   __shared__ float bj[CS];
-  __shared__ float Om[EPI ? CS * DS : 1], rn[EPI ? CS : 1];
+  __shared__ float ssq[EPI ? CS : 1][EPI ? TC : 1];
   const int tid = threadIdx.x;
-  // one (sequence, head) row per workgroup
-  const Row row = st.nseq > 0 ? packed_row(st, blockIdx.x / p.H, blockIdx.x % p.H, p.H, 0, 0)
-                              : uniform_row(blockIdx.x, p.H, p.N, 1, 0);
+  constexpr int SPLIT = D / W;
+  const int r_idx = blockIdx.x / SPLIT;
+  const int c0 = (blockIdx.x % SPLIT) * W;  // first value column of the slice
+  const Row row = st.nseq > 0 ? packed_row(st, r_idx / p.H, r_idx % p.H, p.H, 0, 0)
+                              : uniform_row(r_idx, p.H, p.N, 1, 0);
   const int N = row.len;
   const float sl2 = p.slope[row.h] * kLog2e;
   const size_t head_off = row.tok * D;
@@ -95,82 +114,186 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdPass p, const SeqTable 
   const float* kg = (const float*)p.k + head_off;
   const float* vg = (const float*)p.v + head_off;
   float* og = (float*)p.o + head_off;
-  for (int e = tid; e < D * D; e += 256)
-    Sm[e] = p.state_in ? p.state_in[(size_t)row.st * D * D + e] : 0.f;
   auto tok = [&](int tau) { return p.reverse ? (N - 1 - tau) : tau; };
+
+  // this thread's outputs: rows orow(m) = rg + RG m, columns 4 cg .. +3 of
+  // the slice; its state: rows srow(m) = rg + RG m, same columns
+  const int cg = tid % TC, rg = tid / TC;
+  f32x4_t sv[SR];
+#pragma unroll
+  for (int m = 0; m < SR; ++m) {
+    const int x = rg + RG * m;
+    sv[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (p.state_in && x < D)
+      sv[m] = *reinterpret_cast<const f32x4_t*>(p.state_in + (size_t)row.st * D * D +
+                                                (size_t)x * D + c0 + 4 * cg);
+    if (x < D) *reinterpret_cast<f32x4_t*>(Sm + x * WP + 4 * cg) = sv[m];
+  }
+  // score tile of this thread: rows PB (tid / 16) .., columns PB (tid % 16) ..
+  const int pi0 = PB * (tid >> 4), pj0 = PB * (tid & 15);
+
   for (int t0 = 0; t0 < N; t0 += CS) {
     const int n = min(CS, N - t0);
-    __syncthreads();
-    for (int e = tid; e < CS * D; e += 256) {
-      const int r = e / D, c = e % D;
-      const bool ok = r < n;
-      const size_t g = ok ? (size_t)tok(t0 + r) * D + c : 0;
-      Qm[r * DS + c] = ok ? qg[g] : 0.f;
-      Km[r * DS + c] = ok ? kg[g] : 0.f;
-      Vm[r * DS + c] = ok ? vg[g] : 0.f;
-    }
-    __syncthreads();
-    for (int e = tid; e < CS * CS; e += 256) {
-      const int i = e / CS, j = e % CS;
-      float acc = 0.f;
-      if (j <= i) {
-        for (int x = 0; x < D; ++x) acc = fmaf(Qm[i * DS + x], Km[j * DS + x], acc);
-        acc *= exp2f(-sl2 * (float)(i - j));
+    __syncthreads();  // the previous block is done with Q, K, V, P and S
+    // ---- stage Q, K (all features) and V (the slice) ----
+    for (int e = tid; e < CS * (D / 4); e += 256) {
+      const int r = e / (D / 4), c4 = e % (D / 4);
+      f32x4_t a = {0.f, 0.f, 0.f, 0.f}, b = a;
+      if (r < n) {
+        const size_t g = (size_t)tok(t0 + r) * D + 4 * c4;
+        a = *reinterpret_cast<const f32x4_t*>(qg + g);
+        b = *reinterpret_cast<const f32x4_t*>(kg + g);
       }
-      Pm[i * (CS + 1) + j] = acc;
+      *reinterpret_cast<f32x4_t*>(Qm + r * DP + 4 * c4) = a;
+      *reinterpret_cast<f32x4_t*>(Km + r * DP + 4 * c4) = b;
     }
-    __syncthreads();
-    for (int e = tid; e < CS * D; e += 256) {
-      const int i = e / D, c = e % D;
-      if (i >= n) continue;
-      float intra = 0.f, inter = 0.f;
-      for (int j = 0; j <= i; ++j) intra = fmaf(Pm[i * (CS + 1) + j], Vm[j * DS + c], intra);
-      for (int x = 0; x < D; ++x) inter = fmaf(Qm[i * DS + x], Sm[x * D + c], inter);
-      const float out = intra + exp2f(-sl2 * (float)(i + 1)) * inter;
-      if constexpr (EPI)
-        Om[i * DS + c] = out;
-      else
-        og[(size_t)tok(t0 + i) * D + c] = out;
+    for (int e = tid; e < CS * TC; e += 256) {
+      const int r = e / TC, c4 = e % TC;
+      f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+      if (r < n) a = *reinterpret_cast<const f32x4_t*>(vg + (size_t)tok(t0 + r) * D + c0 + 4 * c4);
+      *reinterpret_cast<f32x4_t*>(Vm + r * WP + 4 * c4) = a;
     }
-    __syncthreads();
-    if constexpr (EPI) {
-      const float* gt = (const float*)p.gate + head_off;
-      if (tid < n) {
-        float ss = 0.f;
-        for (int c = 0; c < D; ++c) ss = fmaf(Om[tid * DS + c], Om[tid * DS + c], ss);
-        rn[tid] = 1.f / sqrtf(ss / (float)D + p.eps);
-      }
-      __syncthreads();
-      for (int e = tid; e < CS * D; e += 256) {
-        const int i = e / D, c = e % D;
-        if (i >= n) continue;
-        const size_t g = (size_t)tok(t0 + i) * D + c;
-        const float sig = 1.f / (1.f + expf(-gt[g]));
-        og[g] = Om[i * DS + c] * rn[i] * p.norm_w[(size_t)row.h * D + c] * sig;
-      }
-    }
-    const float g = exp2f(-sl2 * (float)n);
     if (tid < CS) bj[tid] = tid < n ? exp2f(-sl2 * (float)(n - 1 - tid)) : 0.f;
     __syncthreads();
-    for (int e = tid; e < D * D; e += 256) {
-      const int x = e / D, c = e % D;
-      float acc = 0.f;
-      for (int j = 0; j < n; ++j) acc = fmaf(bj[j] * Km[j * DS + x], Vm[j * DS + c], acc);
-      Sm[e] = fmaf(g, Sm[e], acc);
+    // ---- scores ----
+    {
+      float acc[PB][PB];
+#pragma unroll
+      for (int a = 0; a < PB; ++a)
+#pragma unroll
+        for (int b = 0; b < PB; ++b) acc[a][b] = 0.f;
+#pragma unroll 2
+      for (int x = 0; x < D; x += 4) {
+        f32x4_t qa[PB], kb[PB];
+#pragma unroll
+        for (int a = 0; a < PB; ++a) qa[a] = *reinterpret_cast<const f32x4_t*>(Qm + (pi0 + a) * DP + x);
+#pragma unroll
+        for (int b = 0; b < PB; ++b) kb[b] = *reinterpret_cast<const f32x4_t*>(Km + (pj0 + b) * DP + x);
+#pragma unroll
+        for (int a = 0; a < PB; ++a)
+#pragma unroll
+          for (int b = 0; b < PB; ++b)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[a][b] = fmaf(qa[a][e], kb[b][e], acc[a][b]);
+      }
+#pragma unroll
+      for (int a = 0; a < PB; ++a)
+#pragma unroll
+        for (int b = 0; b < PB; ++b) {
+          const int i = pi0 + a, j = pj0 + b;
+          Pm[i * CP + j] = j <= i ? acc[a][b] * exp2f(-sl2 * (float)(i - j)) : 0.f;
+        }
+    }
+    __syncthreads();
+    // ---- outputs of the slice ----
+    f32x4_t ov[OR];
+#pragma unroll
+    for (int m = 0; m < OR; ++m) {
+      const int i = rg + RG * m;
+      f32x4_t intra = {0.f, 0.f, 0.f, 0.f}, inter = intra;
+      if (i < CS) {
+#pragma unroll 2
+        for (int j = 0; j <= i; j += 4) {
+          const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(Pm + i * CP + j);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const f32x4_t vv = *reinterpret_cast<const f32x4_t*>(Vm + (j + e) * WP + 4 * cg);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) intra[c] = fmaf(pr[e], vv[c], intra[c]);
+          }
+        }
+#pragma unroll 2
+        for (int x = 0; x < D; x += 4) {
+          const f32x4_t qr = *reinterpret_cast<const f32x4_t*>(Qm + i * DP + x);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const f32x4_t sr = *reinterpret_cast<const f32x4_t*>(Sm + (x + e) * WP + 4 * cg);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) inter[c] = fmaf(qr[e], sr[c], inter[c]);
+          }
+        }
+      }
+      const float a_i = exp2f(-sl2 * (float)(i + 1));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ov[m][c] = fmaf(a_i, inter[c], intra[c]);
+    }
+    if constexpr (EPI) {
+      // W == D: the row's TC column groups are TC consecutive threads
+#pragma unroll
+      for (int m = 0; m < OR; ++m) {
+        const int i = rg + RG * m;
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ss = fmaf(ov[m][c], ov[m][c], ss);
+        if (i < CS) ssq[i][cg] = ss;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < OR; ++m) {
+        const int i = rg + RG * m;
+        if (i >= n) continue;
+        float tot = 0.f;
+        for (int g = 0; g < TC; ++g) tot += ssq[i][g];
+        const float rn = 1.f / sqrtf(tot / (float)D + p.eps);
+        const size_t g0 = (size_t)tok(t0 + i) * D + c0 + 4 * cg;
+        const f32x4_t gt = *reinterpret_cast<const f32x4_t*>((const float*)p.gate + head_off + g0);
+        f32x4_t y;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          y[c] = ov[m][c] * rn * p.norm_w[(size_t)row.h * D + c0 + 4 * cg + c] *
+                 (1.f / (1.f + expf(-gt[c])));
+        *reinterpret_cast<f32x4_t*>(og + g0) = y;
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < OR; ++m) {
+        const int i = rg + RG * m;
+        if (i < n) *reinterpret_cast<f32x4_t*>(og + (size_t)tok(t0 + i) * D + c0 + 4 * cg) = ov[m];
+      }
+    }
+    __syncthreads();  // every thread is done reading Sm
+    // ---- state slice: S = lambda^n S + K^T diag(b) V ----
+    const float gdec = exp2f(-sl2 * (float)n);
+#pragma unroll
+    for (int m = 0; m < SR; ++m) {
+      const int x = rg + RG * m;
+      if (x >= D) continue;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int j = 0; j < n; ++j) {
+        const float bk = bj[j] * Km[j * DP + x];
+        const f32x4_t vv = *reinterpret_cast<const f32x4_t*>(Vm + j * WP + 4 * cg);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = fmaf(bk, vv[c], acc[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sv[m][c] = fmaf(gdec, sv[m][c], acc[c]);
+      *reinterpret_cast<f32x4_t*>(Sm + x * WP + 4 * cg) = sv[m];
     }
   }
-  __syncthreads();
-  if (p.state_out)
-    for (int e = tid; e < D * D; e += 256) p.state_out[(size_t)row.st * D * D + e] = Sm[e];
+  if (p.state_out) {
+#pragma unroll
+    for (int m = 0; m < SR; ++m) {
+      const int x = rg + RG * m;
+      if (x < D)
+        *reinterpret_cast<f32x4_t*>(p.state_out + (size_t)row.st * D * D + (size_t)x * D + c0 +
+                                    4 * cg) = sv[m];
+    }
+  }
 }
 
 template <int D, int CS>
 hipError_t launch_f32(const FwdPass& p, const SeqTable& t, hipStream_t s) {
-  const unsigned grid = (unsigned)((t.nseq > 0 ? t.nseq : p.B) * p.H);
+  const unsigned rows = (unsigned)((t.nseq > 0 ? t.nseq : p.B) * p.H);
+  constexpr int W = D < 16 ? D : 16;
+  // the epilogue keeps whole rows (W = D): at d = 128, blocks of 32 rows fit
+  // the LDS
+  constexpr int CSE = D == 128 && CS > 32 ? 32 : CS;
   if (p.gate)
-    hipLaunchKernelGGL((fwd_f32_kernel<D, CS, true>), dim3(grid), dim3(256), 0, s, p, t);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, CSE, D, true>), dim3(rows), dim3(256), 0, s, p, t);
   else
-    hipLaunchKernelGGL((fwd_f32_kernel<D, CS, false>), dim3(grid), dim3(256), 0, s, p, t);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, CS, W, false>), dim3(rows * (D / W)), dim3(256), 0, s,
+                       p, t);
   return hipGetLastError();
 }
 
@@ -183,15 +306,15 @@ hipError_t launch_scan(const ScanPass& p, const SeqTable& t, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Chunks are evaluated in blocks of at most min(C, 64) rows (32 for d = 128);
-// the result does not depend on the blocking beyond rounding.
+// Chunks are evaluated in blocks of min(C, 64) rows; the result does not
+// depend on the blocking beyond rounding.
 hipError_t launch_fwd_f32(const FwdPass& p, const SeqTable& t, hipStream_t s) {
   const int cs = p.C;
   switch (p.D) {
     case 16: return cs >= 64 ? launch_f32<16, 64>(p, t, s) : cs >= 32 ? launch_f32<16, 32>(p, t, s) : launch_f32<16, 16>(p, t, s);
     case 32: return cs >= 64 ? launch_f32<32, 64>(p, t, s) : cs >= 32 ? launch_f32<32, 32>(p, t, s) : launch_f32<32, 16>(p, t, s);
     case 64: return cs >= 64 ? launch_f32<64, 64>(p, t, s) : cs >= 32 ? launch_f32<64, 32>(p, t, s) : launch_f32<64, 16>(p, t, s);
-    case 128: return cs >= 32 ? launch_f32<128, 32>(p, t, s) : launch_f32<128, 16>(p, t, s);
+    case 128: return cs >= 64 ? launch_f32<128, 64>(p, t, s) : cs >= 32 ? launch_f32<128, 32>(p, t, s) : launch_f32<128, 16>(p, t, s);
     default: return hipErrorInvalidValue;
   }
 }
