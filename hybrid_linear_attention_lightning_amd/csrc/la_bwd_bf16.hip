@@ -17,16 +17,19 @@
 //  * wave w owns the d_q columns 32w .. 32w+31 of G (fp32, in registers) and
 //    updates them exactly as the forward kernel updates its state (K^T -> dO
 //    tile, V -> Q fragments);
-//  * the outgoing G is split into bf16 hi + lo both as pass A's A operands
-//    (registers) and, transposed, into an LDS tile G^T (rows d_q) that every
-//    wave reads back with the transposing LDS read as pass B's A operands
-//    for its own d_o columns;
+//  * the outgoing G is split into bf16 hi + lo as pass A's A operands
+//    (registers); after the dK outputs the same values go, transposed, into
+//    an LDS tile G^T (rows d_q) that every wave reads back with the
+//    transposing LDS read as pass B's A operands for its own d_o columns --
+//    in two rounds of d/2 rows, so that the tile needs half the space;
 //  * both passes' masked score tiles are computed once per chunk (waves
 //    0..NW/2-1 take pass A's, the others pass B's) and exchanged through LDS;
 //  * dK and dV are written per query block, dK first.
 // So each chunk updates one state instead of two and reads Q and dO once.
-// The LDS holds four C x d tiles, two score sets and G^T hi/lo: 152 KB at
-// C = 64, d = 128, which is why the fused pass serves chunks of up to 64.
+// The LDS holds the dO and Q tiles, V and K double-buffered (the next
+// chunk's move a whole chunk ahead), two score sets and half of G^T hi/lo:
+// 152 KB at C = 64, d = 128, which is why the fused pass serves chunks of up
+// to 64.
 #include "la_common.h"
 #include "la_internal.h"
 
@@ -51,7 +54,7 @@ struct BCfg {
   static_assert(C == 32 || C == 64, "chunk");
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(C % (RPI * NW) == 0, "whole direct moves per wave");
-  static_assert((4 * TILE + 4 * PT_HALF + 2 * D * D) * 2 <= 160 * 1024, "LDS");
+  static_assert((6 * TILE + 4 * PT_HALF + D * D) * 2 <= 160 * 1024, "LDS");
 };
 
 template <int C, int D>
@@ -135,9 +138,11 @@ __global__ __launch_bounds__(D / 32 * 64) void bwd_kv_bf16_kernel(BwdPass p, con
     return u32x4_t{a[0], a[1], c[0], c[1]};
   };
 
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[G::TILE], Ot[G::TILE], Qt[G::TILE],
-      Kt[G::TILE], PAh[G::PT_HALF], PAl[G::PT_HALF], PBh[G::PT_HALF], PBl[G::PT_HALF],
-      Th[D * D], Tl[D * D];
+  // V and K double-buffered (chunk parity); G^T exchanged in two halves of
+  // D/2 rows (d_q) through Th / Tl
+  __shared__ __attribute__((aligned(16))) uint16_t Ot[G::TILE], Qt[G::TILE], V0[G::TILE],
+      V1[G::TILE], K0[G::TILE], K1[G::TILE], PAh[G::PT_HALF], PAl[G::PT_HALF],
+      PBh[G::PT_HALF], PBl[G::PT_HALF], Th[D * D / 2], Tl[D * D / 2];
 
   // ---- direct global -> LDS moves (reversed rows), as in the forward ------
   constexpr int DM_STEP = G::RPI * G::NW;
@@ -249,21 +254,32 @@ __global__ __launch_bounds__(D / 32 * 64) void bwd_kv_bf16_kernel(BwdPass p, con
     }
   };
 
-  if (tau0 < tau_end) {
-    const int n0 = min(C, tau_end - tau0);
-    load_direct(dog, Ot, tau0, n0);
-    load_direct(qg, Qt, tau0, n0);
-    load_direct(vg, Vt, tau0, n0);
-    load_direct(kg, Kt, tau0, n0);
-  }
-  for (int tc = tau0; tc < tau_end; tc += C) {
+  // One chunk; PAR (the chunk's parity) names this chunk's V and K buffers.
+  // Per chunk: all four tiles have landed at the top (dO and Q were issued
+  // after the previous chunk's scores, V and K a whole chunk ahead); the next
+  // chunk's V and K are issued at once into the other buffers.
+  auto chunk = [&](auto par_c, int tc) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par_c)::value;
+    uint16_t* Vc = PAR ? V1 : V0;
+    uint16_t* Kc = PAR ? K1 : K0;
+    uint16_t* Vn = PAR ? V0 : V1;
+    uint16_t* Kn = PAR ? K0 : K1;
     const int n = min(C, tau_end - tc);
     const bool more = tc + C < tau_end;
     const int n_next = more ? min(C, tau_end - tc - C) : 0;
 #pragma unroll
     for (int ks = 0; ks < G::KSD; ++ks) lA[ks] = opaque(lA[ks]);
-    wait_vmcnt<2 * DM_N>();  // this wave's dO and Q moves are done (V and K may fly)
-    lds_barrier();
+    // vector-memory operations complete in issue order: the tiles of this
+    // chunk were issued before the previous chunk's 2 NQB output stores
+    if (tc == tau0)
+      wait_vmcnt<0>();
+    else
+      wait_vmcnt<2 * G::NQB>();
+    lds_barrier();  // every wave's moves have landed; the previous chunk is done
+    if (more) {
+      load_direct(vg, Vn, tc + C, n_next);
+      load_direct(kg, Kn, tc + C, n_next);
+    }
 
     // Q^T (pass A's V) and dO^T (pass B's V) fragments of this wave's columns
     u32x4_t vfA[G::KSC][CT], vfB[G::KSC][CT];
@@ -275,8 +291,7 @@ __global__ __launch_bounds__(D / 32 * 64) void bwd_kv_bf16_kernel(BwdPass p, con
         vfB[ks][ct] = col_frag(Ot, ks, lV[ct]);
       }
 
-    // outgoing G as hi/lo: pass A's operands in registers, and G^T (rows
-    // d_q = this wave's columns, 4 adjacent d_o per write) for pass B
+    // outgoing G as hi/lo A operands of pass A (registers)
     u32x4_t sfh[CT][G::KSD], sfl[CT][G::KSD];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
@@ -288,10 +303,6 @@ __global__ __launch_bounds__(D / 32 * 64) void bwd_kv_bf16_kernel(BwdPass p, con
         sfh[ct][t >> 1][2 * (t & 1) + 1] = h[1];
         sfl[ct][t >> 1][2 * (t & 1)] = l[0];
         sfl[ct][t >> 1][2 * (t & 1) + 1] = l[1];
-        const int j = col0 + vcol(ct, li);
-        const int off = j * D + 8 * ((4 * (t >> 1) + lg) ^ swz_of<D>(j & 15)) + 4 * (t & 1);
-        *reinterpret_cast<u32x2_t*>(Th + off) = h;
-        *reinterpret_cast<u32x2_t*>(Tl + off) = l;
       }
 
     // G <- lambda^n G + dO^T diag(b) Q (K^T fragments from the dO tile)
@@ -337,9 +348,6 @@ __global__ __launch_bounds__(D / 32 * 64) void bwd_kv_bf16_kernel(BwdPass p, con
       }
     }
 
-    wait_vmcnt<0>();
-    lds_barrier();  // V and K tiles and G^T are in LDS
-
     // score tiles: the first half of the waves pass A's (dO V^T), the others
     // pass B's (Q K^T)
     {
@@ -348,9 +356,9 @@ __global__ __launch_bounds__(D / 32 * 64) void bwd_kv_bf16_kernel(BwdPass p, con
       const int w = passA ? wave : wave - HW;
       for (int pr = w; pr < G::NPAIR; pr += HW) {
         if (passA)
-          pair_tiles(pr, Ot, Vt, PAh, PAl);
+          pair_tiles(pr, Ot, Vc, PAh, PAl);
         else
-          pair_tiles(pr, Qt, Kt, PBh, PBl);
+          pair_tiles(pr, Qt, Kc, PBh, PBl);
       }
     }
 
@@ -361,22 +369,51 @@ __global__ __launch_bounds__(D / 32 * 64) void bwd_kv_bf16_kernel(BwdPass p, con
     }
 
     // dK = pass A's output (its q is V), with G from registers
-    outputs(Vt, sfh, sfl, vfA, PAh, PAl, dkg, tc, n);
-    // dV = pass B's output (its q is K), with G^T read back from LDS
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int ks = 0; ks < G::KSD; ++ks) {
-        sfh[ct][ks] = col_frag(Th, ks, lV[ct]);
-        sfl[ct][ks] = col_frag(Tl, ks, lV[ct]);
-      }
-    outputs(Kt, sfh, sfl, vfB, PBh, PBl, dvg, tc, n);
+    outputs(Vc, sfh, sfl, vfA, PAh, PAl, dkg, tc, n);
 
-    lds_barrier();  // V, K, score and G^T tiles are free for the next chunk
-    if (more) {
-      load_direct(vg, Vt, tc + C, n_next);
-      load_direct(kg, Kt, tc + C, n_next);
+    // G^T for pass B, through LDS in two rounds of D/2 rows (d_q): in round
+    // rd the waves owning d_q rows rd D/2 .. write them (4 adjacent d_o per
+    // write), then every wave reads the fragments of its own d_o columns
+    u32x4_t gh[CT][G::KSD], gl[CT][G::KSD];
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      if (col0 >= rd * (D / 2) && col0 < (rd + 1) * (D / 2)) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int t = 0; t < G::NT; ++t) {
+            const int j = col0 + vcol(ct, li) - rd * (D / 2);
+            const int off = j * D + 8 * ((4 * (t >> 1) + lg) ^ swz_of<D>(j & 15)) + 4 * (t & 1);
+            *reinterpret_cast<u32x2_t*>(Th + off) =
+                u32x2_t{sfh[ct][t >> 1][2 * (t & 1)], sfh[ct][t >> 1][2 * (t & 1) + 1]};
+            *reinterpret_cast<u32x2_t*>(Tl + off) =
+                u32x2_t{sfl[ct][t >> 1][2 * (t & 1)], sfl[ct][t >> 1][2 * (t & 1) + 1]};
+          }
+      }
+      lds_barrier();
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int ks = 0; ks < G::KSD / 2; ++ks) {
+          gh[ct][rd * (G::KSD / 2) + ks] = col_frag(Th, ks, lV[ct]);
+          gl[ct][rd * (G::KSD / 2) + ks] = col_frag(Tl, ks, lV[ct]);
+        }
+      if (rd == 0) lds_barrier();  // the half buffer is read before round 1 rewrites it
     }
+    // dV = pass B's output (its q is K), with G^T from the exchange
+    outputs(Kc, gh, gl, vfB, PBh, PBl, dvg, tc, n);
+  };
+
+  if (tau0 < tau_end) {
+    const int n0 = min(C, tau_end - tau0);
+    load_direct(dog, Ot, tau0, n0);
+    load_direct(qg, Qt, tau0, n0);
+    load_direct(vg, V0, tau0, n0);
+    load_direct(kg, K0, tau0, n0);
+  }
+  for (int tc = tau0; tc < tau_end; tc += 2 * C) {
+    chunk(std::integral_constant<int, 0>{}, tc);
+    if (tc + C < tau_end) chunk(std::integral_constant<int, 1>{}, tc + C);
   }
 }
 
