@@ -351,6 +351,31 @@ def bench_decode(args, torch, la, la_inputs):
     torch.cuda.synchronize()
     cold_us = k0.elapsed_time(k1) * 1e3 / cold_steps
     del Ss
+    # the access pattern's ceiling: a streaming read-modify-write of state-sized
+    # buffers (la_probe_stream_rmw: each float read once and written once, no
+    # arithmetic of the layer), on one buffer and rotating over four, with the
+    # decode kernel's cache policy (nt loads, sc1 stores) and two others
+    probe = {}
+    nf = B * H * d * d
+    policies = (("nt_loads_sc1_stores", la.CPOL_NT, la.CPOL_SC1), ("plain", 0, 0),
+                ("nt_loads_nt_stores", la.CPOL_NT, la.CPOL_NT))
+    for pname, lp, sp in policies:
+        for name, nbuf in (("warm", 1), ("cold", n_rot)):
+            bufs = [torch.ones(nf, dtype=torch.float32, device=dev) for _ in range(nbuf)]
+            for i in range(2 * nbuf):
+                la.probe_stream_rmw(bufs[i % nbuf], 1.0, lp, sp, stream=stream)
+            torch.cuda.synchronize()
+            p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 200
+            p0.record(stream)
+            for i in range(reps):
+                la.probe_stream_rmw(bufs[i % nbuf], 1.0, lp, sp, stream=stream)
+            p1.record(stream)
+            torch.cuda.synchronize()
+            pus = p0.elapsed_time(p1) * 1e3 / reps
+            probe["%s_%s" % (pname, name)] = {"us": pus, "GBs": 2 * nf * 4 / (pus * 1e-6) / 1e9}
+            del bufs
+    ceiling = probe["nt_loads_sc1_stores_cold"]["GBs"]
     res = {
         "B": B, "H": H, "d": d, "steps": steps,
         "us_per_step": us,
@@ -362,11 +387,15 @@ def bench_decode(args, torch, la, la_inputs):
         "copy_GBs": copy_gbs,
         "cold": {"us_per_step": cold_us, "steps": cold_steps,
                  "hbm_frac": bytes_ / (cold_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                 "frac_of_stream_ceiling": bytes_ / (cold_us * 1e-6) / 1e9 / ceiling,
                  "note": "consecutive steps rotating over 4 state copies (537 MB), so no "
                          "step finds its state in the Infinity Cache"},
-        "note": "the 134 MB state fits the 256 MB Infinity Cache, so repeated steps can "
-                "exceed the HBM rate; copy_GBs is a plain 1 GiB device copy (bytes read + "
-                "written per second) for comparison",
+        "stream_rmw_probe": probe,
+        "frac_of_stream_ceiling_warm": achieved / probe["nt_loads_sc1_stores_warm"]["GBs"],
+        "note": "the state is read with nt loads and written with sc1 stores; copy_GBs is a "
+                "plain 1 GiB device copy (bytes read + written per second); stream_rmw_probe "
+                "is la_probe_stream_rmw on state-sized buffers, the ceiling of the same access "
+                "pattern (cold: rotating over 4 buffers)",
     }
     del qs, ks, vs, S, S0
     torch.cuda.empty_cache()
@@ -702,9 +731,11 @@ def main():
     if args.only in (None, "decode"):
         log("decode B=64 ...")
         out["decode"] = bench_decode(args, torch, la, la_inputs)
-        log("  %.2f us/step (graph replay: %s us/step; cold, state evicted: %.2f us/step)" % (
-            out["decode"]["us_per_step"], out["decode"]["graph"]["us_per_step"],
-            out["decode"]["cold"]["us_per_step"]))
+        log("  %.2f us/step (graph replay: %s us/step; cold, state evicted: %.2f us/step; "
+            "streaming ceiling %.0f GB/s)" % (
+                out["decode"]["us_per_step"], out["decode"]["graph"]["us_per_step"],
+                out["decode"]["cold"]["us_per_step"],
+                out["decode"]["stream_rmw_probe"]["nt_loads_sc1_stores_cold"]["GBs"]))
         log("decode 4 tokens per call, B=64 ...")
         out["decode_tokens"] = bench_decode_tokens(args, torch, la, la_inputs)
         log("  %.2f us/call" % out["decode_tokens"]["us_per_call"])

@@ -58,6 +58,7 @@ SIGNATURES = {
     "la_prefill_bwd_varlen": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "la_prefill_bwd_varlen_reuse": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "la_workspace_bytes_varlen": (_Z, [_I, _I, _I, _I, _I, _I, _P]),
+    "la_probe_stream_rmw": (_I, [_P, _Z, ctypes.c_float, _I, _I, _P]),
     "la_status_string": (ctypes.c_char_p, [_I]),
     "la_abi_version": (_I, []),
 }
@@ -440,6 +441,20 @@ def prefill_bwd_varlen(q, k, v, dout, slope, cu_seqlens, chunk=64, dq=None, dk=N
     code = getattr(lib(), fn)(dt, H, d, chunk, nseq, cu, *args, ws, wsb, _stream(stream))
     _check(fn, code)
     return dq, dk, dv
+
+
+CPOL_NT, CPOL_SC1 = 2, 16  # cache-policy bits accepted by probe_stream_rmw
+
+
+def probe_stream_rmw(x, a=1.0, load_policy=CPOL_NT, store_policy=CPOL_SC1, stream=None):
+    """Measurement helper: x <- a x in place over a contiguous fp32 GPU
+    tensor (the decode step's state traffic without its arithmetic), with
+    the given cache-policy bits on the loads and on the stores."""
+    (ptr,) = _ptrs(x.device, (x, "x", x.shape, torch.float32))
+    code = lib().la_probe_stream_rmw(ptr, x.numel(), float(a), int(load_policy),
+                                     int(store_policy), _stream(stream))
+    _check("la_probe_stream_rmw", code)
+    return x
 
 
 def abi_version() -> int:

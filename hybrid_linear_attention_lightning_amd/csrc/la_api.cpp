@@ -770,6 +770,22 @@ size_t la_workspace_bytes(int op, la_dtype_t dt, int B, int H, int N, int d, int
   return make_plan(dt, B, H, N, d, C).ws();
 }
 
+la_status_t la_probe_stream_rmw(float* x, size_t n, float a, int load_policy, int store_policy,
+                                void* stream) {
+  try {
+    if (!x) return LA_ERR_NULL_POINTER;
+    if (load_policy != 0 && load_policy != la::kCpolNt) return LA_ERR_UNSUPPORTED;
+    if (store_policy != 0 && store_policy != la::kCpolNt && store_policy != la::kCpolSc1)
+      return LA_ERR_UNSUPPORTED;
+    if (n == 0 || n % 4 != 0 || n / 4 > (size_t)UINT32_MAX * 1024) return LA_ERR_BAD_SHAPE;
+    if (!aligned16(x)) return LA_ERR_ALIGNMENT;
+    return hip_status(
+        la::launch_stream_rmw(x, n, a, load_policy, store_policy, (hipStream_t)stream));
+  } catch (...) {
+    return LA_ERR_HIP;
+  }
+}
+
 const char* la_status_string(la_status_t s) {
   switch (s) {
     case LA_OK: return "ok";

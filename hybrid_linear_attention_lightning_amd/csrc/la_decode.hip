@@ -17,12 +17,13 @@
 //  * each thread owns 4 adjacent value columns and every RG-th key row,
 //    issues all its 16-byte state loads before any arithmetic and writes the
 //    updated rows back with 16-byte stores;
-//  * the state moves with non-temporal loads and stores: it is read and
-//    written once per step, and between two steps of one layer a model's
-//    other layers evict it from the caches anyway.  Measured on the B=64,
-//    H=32, d=128 step with the state coming from HBM, this is 0.72 of the HBM
-//    peak against 0.63 with ordinary accesses (a plain streaming
-//    read-modify-write kernel reaches 0.75);
+//  * the state is read with non-temporal loads and written with stores that
+//    carry the sc1 cache-policy bit and not nt.  A streaming read-modify-write
+//    of a 134 MB buffer, timed over all 64 combinations of the sc0/sc1/nt
+//    bits, is fast both when the buffer was written just before (0.87 of the
+//    HBM peak: the Infinity Cache serves it) and when it comes from HBM
+//    (0.75) only with nt loads and sc1 stores without nt.  Plain accesses
+//    reach 0.85 and 0.65, nt loads and stores 0.76 and 0.75;
 //  * the partial q^T S column sums of the row groups are reduced across
 //    lanes and then through LDS.
 #include "la_common.h"
@@ -40,12 +41,14 @@ __device__ __forceinline__ float ld_tok<uint16_t>(const uint16_t* p, int i) {
   return bf2f(p[i]);
 }
 
-// Non-temporal 16-byte state accesses (the nt cache-policy bit).
+// 16-byte state accesses: non-temporal loads; stores through a buffer
+// resource over the workgroup's state slice, at byte offset off, with the
+// sc1 cache-policy bit.
 __device__ __forceinline__ f32x4_t ld_state(const float* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
 }
-__device__ __forceinline__ void st_state(float* p, f32x4_t v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
+__device__ __forceinline__ void st_state(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, kCpolSc1);
 }
 
 // Value columns per workgroup.
@@ -77,7 +80,8 @@ __global__ __launch_bounds__(256) void decode_kernel(int H, int K, const T* __re
   const int tid = threadIdx.x;
   const int cg = tid % CG, rg = tid / CG;
   const int lane = tid & 63, wv = tid >> 6;
-  float* S = state + (size_t)bh * D * D + c_base + 4 * cg;
+  float* Sw = state + (size_t)bh * D * D + c_base;  // the workgroup's slice
+  float* S = Sw + 4 * cg;
 
   const bool active = tid < CG * RG;  // all 256 threads unless d < 32
 
@@ -123,8 +127,10 @@ __global__ __launch_bounds__(256) void decode_kernel(int H, int K, const T* __re
         for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
       if (lane < CG) red[j][wv][cg] = acc;
     }
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(Sw);
 #pragma unroll
-    for (int m = 0; m < ROWS; ++m) st_state(S + (size_t)(rg + RG * m) * D, sv[m]);
+    for (int m = 0; m < ROWS; ++m)
+      st_state(rs, (uint32_t)(((rg + RG * m) * D + 4 * cg) * sizeof(float)), sv[m]);
   }
   __syncthreads();
   for (int e = tid; e < K * CG; e += 256) {

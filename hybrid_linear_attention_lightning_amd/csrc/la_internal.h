@@ -178,6 +178,13 @@ hipError_t launch_decode_tokens(bool bf16, int B, int H, int K, int D, const voi
                                 const void* k, const void* v, const float* slope, float* state,
                                 void* o, hipStream_t s);
 
+// Measurement helper (la_probe.hip): x <- a x over n floats in place.  The
+// load policy is 0 or kCpolNt, the store policy 0, kCpolNt or kCpolSc1
+// (cache-policy bits of the buffer instructions).
+constexpr int kCpolNt = 2, kCpolSc1 = 16;
+hipError_t launch_stream_rmw(float* x, size_t n, float a, int load_policy, int store_policy,
+                             hipStream_t s);
+
 // Decay factors below this power of two are treated as exact zeros when a
 // segment start state is assembled from piece states: lambda^dist < 2^-kSkipLog2
 // means the piece contributes less than 2^-32 of its own magnitude, 2^8 below

@@ -363,6 +363,24 @@ la_status_t la_prefill_bwd_varlen_reuse(la_dtype_t dt, int H, int d, int C,
 size_t la_workspace_bytes_varlen(int op, la_dtype_t dt, int H, int d, int C,
                                  int nseq, const int *cu_seqlens);
 
+/* ------------------------------------------------------------------------ *
+ * la_probe_stream_rmw -- measurement helper, not part of the layer: x <- a x
+ * in place over n floats with 16-byte accesses, each element read once and
+ * written once.  It is the decode step's state traffic without its
+ * arithmetic, so its rate is the HBM rate that access pattern can reach on
+ * the GPU it runs on (the ceiling the decode step is compared with).
+ *   x             device pointer, 16-byte aligned
+ *   n             a positive multiple of 4
+ *   load_policy   cache-policy bits of the loads: 0 or LA_CPOL_NT
+ *   store_policy  of the stores: 0, LA_CPOL_NT or LA_CPOL_SC1
+ *                 (the decode kernels use LA_CPOL_NT loads, LA_CPOL_SC1
+ *                 stores); any other value -> LA_ERR_UNSUPPORTED
+ * ------------------------------------------------------------------------ */
+#define LA_CPOL_NT 2
+#define LA_CPOL_SC1 16
+la_status_t la_probe_stream_rmw(float *x, size_t n, float a, int load_policy,
+                                int store_policy, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *la_status_string(la_status_t status);
 

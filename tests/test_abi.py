@@ -202,3 +202,12 @@ def test_noalloc_validation():
     assert call(dt=7) == DTYPE and call(B=0) == SHAPE and call(C=48) == SHAPE
     assert call(q=None) == NULLP and call(q=Q + 8) == ALIGN
     assert call(o=K) == ALIAS and call(s_in=S_IN, s_out=S_IN + 16) == ALIAS
+
+
+def test_probe_validation():
+    f = la.lib().la_probe_stream_rmw
+    assert f(None, 16, 1.0, 2, 16, None) == NULLP
+    assert f(Q, 0, 1.0, 2, 16, None) == SHAPE and f(Q, 6, 1.0, 2, 16, None) == SHAPE
+    assert f(Q + 8, 16, 1.0, 2, 16, None) == ALIGN
+    assert f(Q, 16, 1.0, 1, 16, None) == UNSUP  # sc0 loads are not offered
+    assert f(Q, 16, 1.0, 2, 18, None) == UNSUP  # nor nt|sc1 stores
