@@ -14,11 +14,11 @@
 // where P_p = sum_{t in p} lambda^(end_p - 1 - t) k_t v_t^T and end_p is one
 // past the piece's last token.  A piece whose decay to the next segment start
 // is below 2^-kSkipLog2 is neither computed nor added (its contribution is
-// below fp32 resolution by a factor of more than 2^40).
+// below the fp32 resolution of the sum, which holds the segment's last,
+// undecayed piece as well).
 //
 // fp32 forward.  The chunked recursion evaluated with fp32 FMAs on the vector
-// units, one workgroup per (b, h), chunks of at most 64 (d <= 64) or 32
-// (d = 128) rows so that Q, K, V, the scores and the d x d state fit in LDS.
+// units, one workgroup per (row, slice of value columns); see fwd_f32_kernel.
 #include "la_common.h"
 #include "la_internal.h"
 

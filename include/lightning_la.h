@@ -216,9 +216,10 @@ la_status_t la_decode_step(la_dtype_t dt, int B, int H, int d, const void *q,
  * multi-token generation and the verification of K drafted tokens (the pages
  * serve with multi-token generation, "linghe" section).  Equal to K
  * consecutive la_decode_step calls: token j sees tokens 0..j of the call and
- * the state, and the state advances by all K tokens.  The K tokens are
- * evaluated as one chunk of the prefill form (matrix products for the
- * in-call scores), so the state is read and written once instead of K times.
+ * the state, and the state advances by all K tokens.  Up to 16 tokens run the
+ * recurrence step by step on the state held in registers; more tokens run as
+ * one chunk of the prefill form (matrix products for the in-call scores).
+ * Either way the state is read and written once instead of K times.
  *
  *   dt        LA_F32 or LA_BF16;  B, H >= 1;  1 <= K <= 128 (more gives
  *             LA_ERR_UNSUPPORTED: use la_prefill with state_out = state_in)
