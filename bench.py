@@ -25,7 +25,12 @@ sequence, inputs resident in HBM.  The same line carries:
   * "cpu_baseline": the fp64 CPU oracle on a bounded sample of the headline
     workload (the first tokens of all 32 heads), on the host's cores, with the
     CPU model, the 8K prefill on all cores and on one core, and samples of the
-    decode and training workloads.
+    decode and training workloads;
+  * "power" (with --power): the board power and shader clock the GPU reports
+    (hwmon power1_input, power1_cap and pp_dpm_sclk under /sys/class/drm)
+    while the 128K main prefill kernel, the gated prefill, the decode step
+    (state from HBM) and the streaming probe each run back to back for
+    --power-seconds.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -209,7 +214,7 @@ def bench_tiny_f32(args, torch, la, la_inputs):
     us = e0.elapsed_time(e1) * 1e3 / calls
     return {"B": B, "H": H, "N": N, "d": d, "C": C, "dtype": "f32", "calls": calls,
             "us_per_call": us, "tokens_per_s": B * N / (us * 1e-6),
-            "note": "fwd_f32_kernel, one workgroup per head: bound by launch latency"}
+            "note": "fwd_f32_kernel, one workgroup per (head, 16 value columns): bound by launch latency"}
 
 
 def bench_prefill_gated(args, torch, la, la_inputs):
@@ -670,6 +675,127 @@ def cpu_baseline(args, la_inputs):
     return res
 
 
+def _sysfs_power_files():
+    """hwmon power files and the sclk table of the first card that has them."""
+    import glob
+
+    for card in sorted(glob.glob("/sys/class/drm/card*/device")):
+        inp = sorted(glob.glob(card + "/hwmon/hwmon*/power1_input")) or sorted(
+            glob.glob(card + "/hwmon/hwmon*/power1_average"))
+        if inp:
+            cap = sorted(glob.glob(card + "/hwmon/hwmon*/power1_cap"))
+            return inp[0], cap[0] if cap else None, card + "/pp_dpm_sclk"
+    return None, None, None
+
+
+def bench_power(args, torch, la, la_inputs):
+    """Board power and shader clock while one kernel runs back to back: the
+    GPU's own hwmon readings (microwatts) and its current sclk level, sampled
+    every 50 ms from another thread, averaged over the steady part of each
+    phase.  None if the files cannot be read."""
+    import threading
+
+    f_in, f_cap, f_sclk = _sysfs_power_files()
+    if f_in is None:
+        return None
+
+    def read(f):
+        try:
+            with open(f) as fh:
+                return fh.read()
+        except OSError:
+            return None
+
+    if read(f_in) is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            p_ = read(f_in)
+            sc = read(f_sclk) or ""
+            cur = [ln for ln in sc.splitlines() if ln.strip().endswith("*")]
+            mhz = None
+            if cur:
+                try:
+                    mhz = float(cur[0].split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+                except (IndexError, ValueError):
+                    mhz = None
+            samples.append((time.time(), float(p_) / 1e6 if p_ else None, mhz))
+            time.sleep(0.05)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    phases = {}
+
+    def phase(name, fn):
+        torch.cuda.synchronize()
+        t0 = time.time()
+        calls = 0
+        while time.time() - t0 < args.power_seconds:
+            for _ in range(10):
+                fn()
+            calls += 10
+            torch.cuda.synchronize()
+        t1 = time.time()
+        rows = [r for r in samples if t0 + 0.5 <= r[0] <= t1]
+        pw = [r[1] for r in rows if r[1] is not None]
+        mz = [r[2] for r in rows if r[2] is not None]
+        phases[name] = {"board_W": sum(pw) / len(pw) if pw else None,
+                        "board_W_max": max(pw) if pw else None,
+                        "sclk_MHz": sum(mz) / len(mz) if mz else None,
+                        "samples": len(rows), "calls": calls,
+                        "ms_per_call": (t1 - t0) * 1e3 / calls}
+
+    time.sleep(1.0)
+    idle = [r[1] for r in samples if r[1] is not None]
+    c = la_inputs.CONFIGS["prefill_128k"]
+    B, H, N, d, C = c["B"], c["H"], c["N"], c["d"], c["C"]
+    q, k, v = la_inputs.qkv_device(c["seed"], B, H, N, d, dev, torch.bfloat16)
+    slope = torch.from_numpy(la_inputs.slopes(H)).to(dev)
+    o = torch.empty_like(q)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(la.workspace_bytes(0, la.LA_BF16, B, H, N, d, C), dtype=torch.uint8,
+                     device=dev)
+    la.prefill_prepass(k, v, slope, C, ws, stream=stream)
+    phase("prefill_main_128k",
+          lambda: la.prefill_main(q, k, v, slope, C, ws, o, state_out=S, stream=stream))
+    g = la_inputs.gate_device(c["seed"], B, H, N, d, dev, torch.bfloat16)
+    w = torch.from_numpy(la_inputs.norm_weight(c["seed"], H, d)).to(dev)
+    phase("prefill_gated_128k",
+          lambda: la.prefill_gated(q, k, v, slope, g, w, chunk=C, out=o, state_out=S,
+                                   workspace=ws, stream=stream))
+    del g, o, ws
+    Bd, Hd = 64, 32
+    S0 = torch.from_numpy(la_inputs.decode_state(3, Bd, Hd, d)).to(dev)
+    Ss = [S0.clone() for _ in range(4)]
+    qd = (torch.randn((Bd, Hd, d), device=dev) / d ** 0.5).to(torch.bfloat16)
+    sd = torch.from_numpy(la_inputs.slopes(Hd)).to(dev)
+    od = torch.empty_like(qd)
+    step = [0]
+
+    def dstep():
+        step[0] += 1
+        la.decode_step(qd, qd, qd, sd, Ss[step[0] % 4], out=od, stream=stream)
+
+    phase("decode_state_from_hbm", dstep)
+    del Ss, S0
+    x = torch.ones(B * H * N * d // 2, dtype=torch.float32, device=dev)  # q, k, v's size
+    phase("stream_rmw_probe", lambda: la.probe_stream_rmw(x, 1.0, stream=stream))
+    stop.set()
+    th.join()
+    del q, k, v, x
+    torch.cuda.empty_cache()
+    cap = read(f_cap) if f_cap else None
+    return {"cap_W": float(cap) / 1e6 if cap else None,
+            "idle_W": sum(idle) / len(idle) if idle else None,
+            "seconds_per_phase": args.power_seconds,
+            "phases": phases,
+            "source": f_in}
+
+
 def copy_calibration(torch):
     """A plain 1 GiB device-to-device copy, for scaling HBM counters."""
     dev = torch.device("cuda:0")
@@ -695,6 +821,9 @@ def main():
                     help="run one workload only (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB copy (HBM counter calibration)")
+    ap.add_argument("--power", action="store_true",
+                    help="also sample board power and shader clock per kernel")
+    ap.add_argument("--power-seconds", type=float, default=3.0)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -747,6 +876,14 @@ def main():
         log("varlen fwd+bwd, 64 packed sequences, T=128K ...")
         out["varlen"] = bench_varlen(args, torch, la, la_inputs)
         log("  fwd %.3f ms, bwd %.3f ms" % (out["varlen"]["fwd_ms"], out["varlen"]["bwd_ms"]))
+    if args.power:
+        log("board power per kernel ...")
+        out["power"] = bench_power(args, torch, la, la_inputs)
+        if out["power"]:
+            log("  " + ", ".join("%s %.0f W at %s MHz" % (k_, v_["board_W"] or 0, v_["sclk_MHz"])
+                                 for k_, v_ in out["power"]["phases"].items()))
+        else:
+            log("  no readable power sensor")
     cpu = None
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         log("cpu baseline (oracle) ...")
@@ -780,6 +917,8 @@ def main():
         "train": out.get("train"),
         "varlen": out.get("varlen"),
     }
+    if args.power:
+        line["power"] = out.get("power")
     print(json.dumps(line), flush=True)
 
 
