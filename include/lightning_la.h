@@ -202,9 +202,10 @@ la_status_t la_prefill_main(la_dtype_t dt, int B, int H, int N, int d, int C,
  *   B, H      >= 1, B*H at most 2^30 (LA_ERR_UNSUPPORTED above)
  *   q, k, v   [B][H][d] of dt
  *   slope     [H] fp32
- *   state     [B][H][d][d] fp32, read and written in place with
- *             non-temporal accesses (streamed from and to HBM, not kept in
- *             the caches)
+ *   state     [B][H][d][d] fp32, read and written in place: read with
+ *             non-temporal loads, written with sc1 stores (so that a state
+ *             the Infinity Cache still holds is read from it, and one it
+ *             does not hold streams from HBM at the full rate)
  *   o         [B][H][d] of dt, written; must not overlap q, k, v or state
  * ------------------------------------------------------------------------ */
 la_status_t la_decode_step(la_dtype_t dt, int B, int H, int d, const void *q,
