@@ -66,7 +66,7 @@ MARGINS = {}
 
 def _record(what, got, ref, dtype, stored_bf16, r):
     test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
-    key = "%s :: %s" % (test, (what.split() or ["?"])[0])
+    key = "%s :: %s" % (test, what)
     m = MARGINS.setdefault(key, {"ratio": 0.0, "ratio_no_allowance": 0.0, "checks": 0})
     m["ratio"] = max(m["ratio"], r)
     m["checks"] += 1
