@@ -325,8 +325,8 @@ def bench_decode(args, torch, la, la_inputs):
     o = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
     S = S0.clone()
     stream = torch.cuda.current_stream()
-    for i in range(min(10, steps)):
-        la.decode_step(qs[i], ks[i], vs[i], slope, S, out=o, stream=stream)
+    for i in range(200):  # untimed: the clock settles
+        la.decode_step(qs[i % steps], ks[i % steps], vs[i % steps], slope, S, out=o, stream=stream)
     S.copy_(S0)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -437,8 +437,8 @@ def bench_decode_tokens(args, torch, la, la_inputs):
     o = torch.empty((B, H, K, d), dtype=torch.bfloat16, device=dev)
     S = S0.clone()
     stream = torch.cuda.current_stream()
-    for i in range(10):
-        la.decode_tokens(qs[i], ks[i], vs[i], slope, S, out=o, stream=stream)
+    for i in range(200):  # untimed: the clock settles
+        la.decode_tokens(qs[i % calls], ks[i % calls], vs[i % calls], slope, S, out=o, stream=stream)
     S.copy_(S0)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -490,7 +490,7 @@ def bench_train(args, torch, la, la_inputs):
         if e is not None:
             e[2].record(stream)
 
-    for _ in range(2):
+    for _ in range(20):  # untimed: the clock settles
         step()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
@@ -548,7 +548,7 @@ def bench_varlen(args, torch, la, la_inputs):
         if e is not None:
             e[2].record(stream)
 
-    for _ in range(2):
+    for _ in range(20):  # untimed: the clock settles
         step()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
@@ -827,7 +827,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed steps first: the clock settles at the power limit within tens of ms")
     ap.add_argument("--decode-steps", type=int, default=1000)
-    ap.add_argument("--train-steps", type=int, default=3)
+    ap.add_argument("--train-steps", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "small", "decode", "train", "varlen"],
