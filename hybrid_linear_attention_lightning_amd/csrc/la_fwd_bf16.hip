@@ -134,8 +134,17 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
     // a real segment start and the decay over the gap is not negligible
     const int r_star = (tau_end + pp.seg_len - 1) / pp.seg_len;
     if (tau0 >= tau_end || r_star > row.nseg - 1) return;
+    const float rate = slope[row.h] * kLog2e;  // log2 of the decay per token
     const float gap = (float)(r_star * pp.seg_len - tau_end);
-    if (slope[row.h] * kLog2e * gap >= kSkipLog2) return;
+    if (rate * gap >= kSkipLog2) return;
+    // by the same rule, the piece's tokens whose decay to that segment start
+    // is below 2^-kSkipLog2 are not accumulated: the pass starts at the
+    // chunk that holds the earliest token above it
+    if (rate * (float)(tau_end - tau0) > kSkipLog2) {
+      const int keep = (int)(kSkipLog2 / rate) + 1;  // < tau_end - tau0 + gap here
+      const int first = r_star * pp.seg_len - keep;  // earliest token kept
+      if (first > tau0) tau0 += ((first - tau0) / C) * C;
+    }
     const size_t head_off = row.tok * D;
     kg = (const uint16_t*)pp.k + head_off;
     vg = (const uint16_t*)pp.v + head_off;
