@@ -29,8 +29,8 @@ sequence, inputs resident in HBM.  The same line carries:
   * "power" (with --power): the board power and shader clock the GPU reports
     (hwmon power1_input, power1_cap and pp_dpm_sclk under /sys/class/drm)
     while the 128K main prefill kernel, the gated prefill, the decode step
-    (state from HBM) and the streaming probe each run back to back for
-    --power-seconds.
+    (state from HBM), the training backward and the streaming probe each run
+    back to back for --power-seconds.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -795,6 +795,21 @@ def bench_power(args, torch, la, la_inputs):
 
     phase("decode_state_from_hbm", dstep)
     del Ss, S0
+    # training backward (B=4, H=16, N=32768, chunk 64) on the forward's workspace
+    Bt, Ht, Nt, Ct = 4, 16, 32768, 64
+    qt, kt, vt = la_inputs.qkv_device(4, Bt, Ht, Nt, d, dev, torch.bfloat16)
+    gt = la_inputs.upstream_grad_device(4, Bt, Ht, Nt, d, dev, torch.bfloat16)
+    st = torch.from_numpy(la_inputs.slopes(Ht)).to(dev)
+    ot = torch.empty_like(qt)
+    dq, dk, dv = torch.empty_like(qt), torch.empty_like(qt), torch.empty_like(qt)
+    wst = torch.empty(max(la.workspace_bytes(0, la.LA_BF16, Bt, Ht, Nt, d, Ct),
+                          la.workspace_bytes(1, la.LA_BF16, Bt, Ht, Nt, d, Ct)),
+                      dtype=torch.uint8, device=dev)
+    la.prefill(qt, kt, vt, st, chunk=Ct, out=ot, return_state=False, workspace=wst, stream=stream)
+    phase("train_backward",
+          lambda: la.prefill_bwd(qt, kt, vt, gt, st, chunk=Ct, dq=dq, dk=dk, dv=dv, workspace=wst,
+                                 stream=stream, reuse_forward_workspace=True))
+    del qt, kt, vt, gt, ot, dq, dk, dv, wst
     x = torch.ones(B * H * N * d // 2, dtype=torch.float32, device=dev)  # q, k, v's size
     phase("stream_rmw_probe", lambda: la.probe_stream_rmw(x, 1.0, stream=stream))
     stop.set()
