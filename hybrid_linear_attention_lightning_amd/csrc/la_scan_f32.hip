@@ -132,27 +132,52 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdPass p, const SeqTable 
   // score tile of this thread: rows PB (tid / 16) .., columns PB (tid % 16) ..
   const int pi0 = PB * (tid >> 4), pj0 = PB * (tid & 15);
 
+  // Q, K (all features) and V (the slice) of a block move global ->
+  // registers -> LDS; the next block's loads are issued as soon as the
+  // current block is in LDS, so they are in flight during its arithmetic.
+  constexpr int QK_IT = (CS * (D / 4) + 255) / 256;  // float4 per thread
+  constexpr int V_IT = (CS * TC + 255) / 256;
+  f32x4_t qr[QK_IT], kr[QK_IT], vr[V_IT];
+  auto fetch = [&](int t0) {
+    const int n = min(CS, N - t0);
+#pragma unroll
+    for (int it = 0; it < QK_IT; ++it) {
+      const int e = tid + 256 * it, r = e / (D / 4), c4 = e % (D / 4);
+      qr[it] = kr[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (e < CS * (D / 4) && r < n) {
+        const size_t g = (size_t)tok(t0 + r) * D + 4 * c4;
+        qr[it] = *reinterpret_cast<const f32x4_t*>(qg + g);
+        kr[it] = *reinterpret_cast<const f32x4_t*>(kg + g);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < V_IT; ++it) {
+      const int e = tid + 256 * it, r = e / TC, c4 = e % TC;
+      vr[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (e < CS * TC && r < n)
+        vr[it] = *reinterpret_cast<const f32x4_t*>(vg + (size_t)tok(t0 + r) * D + c0 + 4 * c4);
+    }
+  };
+  if (N > 0) fetch(0);
+
   for (int t0 = 0; t0 < N; t0 += CS) {
     const int n = min(CS, N - t0);
     __syncthreads();  // the previous block is done with Q, K, V, P and S
-    // ---- stage Q, K (all features) and V (the slice) ----
-    for (int e = tid; e < CS * (D / 4); e += 256) {
-      const int r = e / (D / 4), c4 = e % (D / 4);
-      f32x4_t a = {0.f, 0.f, 0.f, 0.f}, b = a;
-      if (r < n) {
-        const size_t g = (size_t)tok(t0 + r) * D + 4 * c4;
-        a = *reinterpret_cast<const f32x4_t*>(qg + g);
-        b = *reinterpret_cast<const f32x4_t*>(kg + g);
+    // ---- stage this block's Q, K, V; start the next block's loads ----
+#pragma unroll
+    for (int it = 0; it < QK_IT; ++it) {
+      const int e = tid + 256 * it, r = e / (D / 4), c4 = e % (D / 4);
+      if (e < CS * (D / 4)) {
+        *reinterpret_cast<f32x4_t*>(Qm + r * DP + 4 * c4) = qr[it];
+        *reinterpret_cast<f32x4_t*>(Km + r * DP + 4 * c4) = kr[it];
       }
-      *reinterpret_cast<f32x4_t*>(Qm + r * DP + 4 * c4) = a;
-      *reinterpret_cast<f32x4_t*>(Km + r * DP + 4 * c4) = b;
     }
-    for (int e = tid; e < CS * TC; e += 256) {
-      const int r = e / TC, c4 = e % TC;
-      f32x4_t a = {0.f, 0.f, 0.f, 0.f};
-      if (r < n) a = *reinterpret_cast<const f32x4_t*>(vg + (size_t)tok(t0 + r) * D + c0 + 4 * c4);
-      *reinterpret_cast<f32x4_t*>(Vm + r * WP + 4 * c4) = a;
+#pragma unroll
+    for (int it = 0; it < V_IT; ++it) {
+      const int e = tid + 256 * it, r = e / TC, c4 = e % TC;
+      if (e < CS * TC) *reinterpret_cast<f32x4_t*>(Vm + r * WP + 4 * c4) = vr[it];
     }
+    if (t0 + CS < N) fetch(t0 + CS);
     if (tid < CS) bj[tid] = tid < n ? exp2f(-sl2 * (float)(n - 1 - tid)) : 0.f;
     __syncthreads();
     // ---- scores ----
