@@ -59,8 +59,11 @@ constexpr int decode_cols() { return D < 64 ? D : 64; }
 // o_j = q_j^T S_j, the K steps of the recurrence on a state held in
 // registers, so the state is streamed once for all K tokens.  Workgroup
 // (b h) * SPLIT + part owns value columns part * COLS .. +COLS-1.
+// Threads per workgroup: 512 (8 waves) measured 1% faster than 256 and 4%
+// faster than 128 on the B=64, H=32, d=128 step with the state from HBM.
+constexpr int kDecThreads = 512;
 template <int D, typename T, int KMAX>
-__global__ __launch_bounds__(256) void decode_kernel(int H, int K, const T* __restrict__ q,
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(int H, int K, const T* __restrict__ q,
                                                     const T* __restrict__ k,
                                                     const T* __restrict__ v,
                                                     const float* __restrict__ slope,
@@ -68,7 +71,7 @@ __global__ __launch_bounds__(256) void decode_kernel(int H, int K, const T* __re
   constexpr int COLS = decode_cols<D>();
   constexpr int SPLIT = D / COLS;  // workgroups per (b, h)
   constexpr int CG = COLS / 4;     // float4 column groups
-  constexpr int RG = (256 / CG < D) ? 256 / CG : D;  // row groups
+  constexpr int RG = (kDecThreads / CG < D) ? kDecThreads / CG : D;  // row groups
   constexpr int ROWS = D / RG;     // rows per thread
   constexpr int NWV = (CG * RG + 63) / 64;           // active waves
   __shared__ float qs[KMAX][D], ks[KMAX][D], vs[KMAX][COLS];
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(256) void decode_kernel(int H, int K, const T* __re
   float* Sw = state + (size_t)bh * D * D + c_base;  // the workgroup's slice
   float* S = Sw + 4 * cg;
 
-  const bool active = tid < CG * RG;  // all 256 threads unless d < 32
+  const bool active = tid < CG * RG;  // every thread unless d < 64
 
   // issue the state loads first: they are the whole cost
   f32x4_t sv[ROWS];
@@ -93,12 +96,12 @@ __global__ __launch_bounds__(256) void decode_kernel(int H, int K, const T* __re
   }
 
   const size_t tok0 = (size_t)bh * K * D;
-  for (int e = tid; e < K * D; e += 256) {
+  for (int e = tid; e < K * D; e += kDecThreads) {
     const int j = e / D, c = e - j * D;
     qs[j][c] = ld_tok(q + tok0, e);
     ks[j][c] = ld_tok(k + tok0, e);
   }
-  for (int e = tid; e < K * COLS; e += 256) {
+  for (int e = tid; e < K * COLS; e += kDecThreads) {
     const int j = e / COLS, c = e - j * COLS;
     vs[j][c] = ld_tok(v + tok0, j * D + c_base + c);
   }
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(256) void decode_kernel(int H, int K, const T* __re
       st_state(rs, (uint32_t)(((rg + RG * m) * D + 4 * cg) * sizeof(float)), sv[m]);
   }
   __syncthreads();
-  for (int e = tid; e < K * CG; e += 256) {
+  for (int e = tid; e < K * CG; e += kDecThreads) {
     const int j = e / CG, c4 = e - j * CG;
     f32x4_t t = red[j][0][c4];
 #pragma unroll
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(256) void decode_kernel(int H, int K, const T* __re
 template <int D, int KMAX>
 hipError_t launch_d(bool bf16, int B, int H, int K, const void* q, const void* k, const void* v,
                     const float* slope, float* state, void* o, hipStream_t s) {
-  const dim3 grid((unsigned)(B * H * (D / decode_cols<D>()))), block(256);
+  const dim3 grid((unsigned)(B * H * (D / decode_cols<D>()))), block(kDecThreads);
   if (bf16)
     hipLaunchKernelGGL((decode_kernel<D, uint16_t, KMAX>), grid, block, 0, s, H, K,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, slope, state,
