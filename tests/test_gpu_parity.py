@@ -118,6 +118,24 @@ def test_state_continuation_and_in_place(oracle_mod):
     assert_close(to_host(S2), rS, "bf16", "S", stored_bf16=False)
 
 
+def test_pieces_truncated_by_decay(oracle_mod):
+    """64 rows of 8192 tokens: four segments of 2048 tokens per row, cut into
+    two pieces of 1024 for the pre-pass.  For the faster heads only the last
+    tokens of the piece before a segment start carry a decay above 2^-32
+    (32 tokens for head 0 at H = 16), so the piece pass starts near the end
+    of its piece; the slowest heads use whole pieces.  Every row against the
+    oracle, from an initial state."""
+    B, H, N, d, C = 4, 16, 8192, 64, 64
+    assert la.workspace_bytes(0, la.LA_BF16, B, H, N, d, C) > 0  # a segmented plan
+    q, k, v = _inputs(808, B, H, N, d, "bf16")
+    s = la_inputs.slopes(H)
+    S0 = la_inputs.decode_state(808, B, H, d)
+    o, S = _run_prefill(q, k, v, s, C, "bf16", S0)
+    ro, rS = oracle_mod.fwd(q, k, v, s, S0)
+    assert_close(o, ro, "bf16", "o")
+    assert_close(S, rS, "bf16", "S", stored_bf16=False)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_decode_steps(oracle_mod, dtype):
     B, H, d, steps = 3, 4, 128 if dtype == "bf16" else 64, 5
