@@ -26,7 +26,7 @@ sequence, inputs resident in HBM.  The same line carries:
     workload (the first tokens of all 32 heads), on the host's cores, with the
     CPU model, the 8K prefill on all cores and on one core, and samples of the
     decode and training workloads;
-  * "power" (with --power): the board power and shader clock the GPU reports
+  * "power" (unless --no-power or --only): the board power and shader clock the GPU reports
     (hwmon power1_input, power1_cap and pp_dpm_sclk under /sys/class/drm)
     while the 128K main prefill kernel, the gated prefill, the decode step
     (state from HBM), the training backward and the streaming probe each run
@@ -850,9 +850,9 @@ def main():
                     help="run one workload only (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB copy (HBM counter calibration)")
-    ap.add_argument("--power", action="store_true",
-                    help="also sample board power and shader clock per kernel")
-    ap.add_argument("--power-seconds", type=float, default=3.0)
+    ap.add_argument("--no-power", dest="power", action="store_false",
+                    help="skip sampling board power and shader clock per kernel")
+    ap.add_argument("--power-seconds", type=float, default=2.0)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -905,7 +905,7 @@ def main():
         log("varlen fwd+bwd, 64 packed sequences, T=128K ...")
         out["varlen"] = bench_varlen(args, torch, la, la_inputs)
         log("  fwd %.3f ms, bwd %.3f ms" % (out["varlen"]["fwd_ms"], out["varlen"]["bwd_ms"]))
-    if args.power:
+    if args.power and args.only is None:
         log("board power per kernel ...")
         out["power"] = bench_power(args, torch, la, la_inputs)
         if out["power"]:
@@ -946,8 +946,8 @@ def main():
         "train": out.get("train"),
         "varlen": out.get("varlen"),
     }
-    if args.power:
-        line["power"] = out.get("power")
+    if "power" in out:
+        line["power"] = out["power"]
     print(json.dumps(line), flush=True)
 
 
