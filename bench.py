@@ -11,7 +11,7 @@ sequence, inputs resident in HBM.  The same line carries:
   * "prefill_8k": the 8K-token prefill (B=1, H=32, N=8192, d=128, chunk 64),
     timed and reported like the headline;
   * "tiny_f32": the tiny fp32 prefill (B=1, H=2, N=256, d=64, chunk 64),
-    microseconds per call;
+    microseconds per call, back to back and replayed from a HIP graph;
   * "decode": the batched decode step (B=64, H=32, d=128), 1000 consecutive
     steps with fresh q/k/v each, microseconds per step and HBM fraction;
   * "prefill_gated": the same prefill with the fused output epilogue
@@ -205,7 +205,8 @@ def bench_prefill(args, torch, la, la_inputs, name="prefill_128k"):
 
 def bench_tiny_f32(args, torch, la, la_inputs):
     """The tiny fp32 workload (B=1, H=2, N=256, d=64, chunk 64): microseconds
-    per la_prefill call, back to back (launch-latency bound)."""
+    per la_prefill call, back to back from Python and replayed from a HIP
+    graph (the replayed outputs are checked bit for bit against eager ones)."""
     c = la_inputs.CONFIGS["tiny_f32"]
     B, H, N, d, C = c["B"], c["H"], c["N"], c["d"], c["C"]
     dev = torch.device("cuda:0")
@@ -225,9 +226,37 @@ def bench_tiny_f32(args, torch, la, la_inputs):
     e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / calls
+    o_eager, S_eager = o.clone(), S.clone()
+    # the same call captured n times in one graph, replayed
+    n, reps = 50, 20
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        o.zero_()
+        S.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(n):
+                la.prefill(q, k, v, slope, chunk=C, out=o, state_out=S, stream=side)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    us_graph = None
+    if torch.equal(o, o_eager) and torch.equal(S, S_eager):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us_graph = e0.elapsed_time(e1) * 1e3 / (reps * n)
     return {"B": B, "H": H, "N": N, "d": d, "C": C, "dtype": "f32", "calls": calls,
             "us_per_call": us, "tokens_per_s": B * N / (us * 1e-6),
-            "note": "fwd_f32_kernel, one workgroup per (head, 16 value columns): bound by launch latency"}
+            "us_per_call_graph": us_graph, "calls_per_graph": n, "replays": reps,
+            "note": "fwd_f32_quad_kernel: rows of at most 256 tokens in the parallel form, one "
+                    "workgroup per 16 query rows and per 16 state rows (40 here); us_per_call: "
+                    "calls back to back from Python, us_per_call_graph: the same call replayed "
+                    "from a HIP graph (null if a replay differed from the eager result)"}
 
 
 def bench_prefill_gated(args, torch, la, la_inputs):
@@ -885,7 +914,8 @@ def main():
         log("  %.1f us/step" % (out["prefill_8k"]["ms_per_step"] * 1e3))
         log("tiny fp32 prefill ...")
         out["tiny_f32"] = bench_tiny_f32(args, torch, la, la_inputs)
-        log("  %.1f us/call" % out["tiny_f32"]["us_per_call"])
+        log("  %.1f us/call (graph replay: %s us/call)" % (out["tiny_f32"]["us_per_call"],
+                                                           out["tiny_f32"]["us_per_call_graph"]))
     if args.only in (None, "decode"):
         log("decode B=64 ...")
         out["decode"] = bench_decode(args, torch, la, la_inputs)

@@ -165,6 +165,9 @@ __host__ __device__ inline int seq_of_segment(const SeqTable& t, int g) {
 }
 
 hipError_t launch_fwd_bf16(const FwdPass& p, const SeqTable& t, hipStream_t s);
+// fp32 forward; forward rows of at most kQuadMaxN tokens (uniform layout, no
+// epilogue) are evaluated in the parallel form, longer ones chunk by chunk.
+constexpr int kQuadMaxN = 256;
 hipError_t launch_fwd_f32(const FwdPass& p, const SeqTable& t, hipStream_t s);
 hipError_t launch_pieces_bf16(const PiecePass& p, const SeqTable& t, hipStream_t s);
 hipError_t launch_scan(const ScanPass& p, const SeqTable& t, hipStream_t s);

@@ -74,7 +74,10 @@ typedef enum {
  * and the chunk reads the d x d state carried from the previous chunks (the
  * evaluation order described on the "Context Parallel for Lightning
  * Attention" section: a local recursion, unfolded into matrix form, plus the
- * carried state).  C changes only the rounding, never the result.
+ * carried state).  C changes only the rounding, never the result.  LA_F32
+ * rows of at most 256 tokens are evaluated as one masked product over the
+ * whole row (the same sum, with no chunk recursion), except an in-place
+ * continuation, which runs chunked.
  *
  *   dt        LA_F32 or LA_BF16 (type of q, k, v, o)
  *   B, H, N   >= 1;  d in {64, 128} (LA_F32 also allows 16 and 32)

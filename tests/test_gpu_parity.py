@@ -87,6 +87,47 @@ def test_f32_prefill(oracle_mod, B, H, N, d, C, with_state):
     assert_close(S, rS, "f32", "S", stored_bf16=False)
 
 
+# fp32 rows of at most 256 tokens take the parallel form (one workgroup per
+# 16 query rows and per 16 state rows), longer rows the chunked kernel: the
+# cases straddle the 16-row blocks, the 64-key steps and the 256-token switch.
+F32_SHORT_CASES = [(N, d) for d in (16, 64, 128) for N in (15, 17, 64, 65, 256, 257)] + [
+    (1, 32), (200, 32)]
+
+
+@pytest.mark.parametrize("N,d", F32_SHORT_CASES)
+def test_f32_short_rows(oracle_mod, N, d):
+    B, H, C = 2, 2, 64
+    q, k, v = _inputs(500 + N + d, B, H, N, d, "f32")
+    s = la_inputs.slopes(H)
+    S0 = la_inputs.decode_state(9, B, H, d)
+    o, S = _run_prefill(q, k, v, s, C, "f32", S0)
+    ro, rS = oracle_mod.fwd(q, k, v, s, S0)
+    assert_close(o, ro, "f32", "o")
+    assert_close(S, rS, "f32", "S", stored_bf16=False)
+
+
+def test_f32_short_rows_without_state_and_in_place(oracle_mod):
+    B, H, N, d, C = 1, 4, 100, 64, 32
+    q, k, v = _inputs(531, B, H, N, d, "f32")
+    s = np.array([0.0, 1.0e4, 2.0**-8, 0.9], dtype=np.float32)  # degenerate decays too
+    tq, tk, tv = (to_dev(x, "f32") for x in (q, k, v))
+    ts = torch.from_numpy(s).to(device())
+    # no state in or out: only the query-block workgroups run
+    o, none = la.prefill(tq, tk, tv, ts, chunk=C, return_state=False)
+    torch.cuda.synchronize()
+    assert none is None
+    ro, rS = oracle_mod.fwd(q, k, v, s)
+    assert_close(to_host(o), ro, "f32", "o")
+    # an in-place continuation (state_in is state_out) keeps the chunked kernel
+    S0 = la_inputs.decode_state(10, B, H, d)
+    tS = torch.from_numpy(np.ascontiguousarray(S0, dtype=np.float32)).to(device())
+    o2, S2 = la.prefill(tq, tk, tv, ts, chunk=C, state_in=tS, state_out=tS)
+    torch.cuda.synchronize()
+    ro2, rS2 = oracle_mod.fwd(q, k, v, s, S0)
+    assert_close(to_host(o2), ro2, "f32", "o in place")
+    assert_close(to_host(S2), rS2, "f32", "S in place", stored_bf16=False)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_degenerate_decays(oracle_mod, dtype):
     # slope 0 (no decay: every earlier token counts, no piece may be skipped),
