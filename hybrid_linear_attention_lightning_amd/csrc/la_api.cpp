@@ -221,8 +221,10 @@ la_status_t scratch_address(void** out) {
 la_status_t check_seq(la_dtype_t dt, int B, int H, int N, int d, int C) {
   if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_BAD_DTYPE;
   if (B < 1 || H < 1 || N < 1 || !d_ok(dt, d) || !c_ok(C)) return LA_ERR_BAD_SHAPE;
-  // int indexing of grids and token offsets inside the kernels
+  // int indexing of grids and token offsets inside the kernels: token
+  // offsets below 2^30 and grids of at most 24 workgroups per row below 2^31
   if ((long long)B * H * N > (1LL << 31) / 2) return LA_ERR_UNSUPPORTED;
+  if ((long long)B * H > (1LL << 26)) return LA_ERR_UNSUPPORTED;
   return LA_OK;
 }
 

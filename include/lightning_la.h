@@ -84,8 +84,8 @@ typedef enum {
  *   C         chunk length, one of {16, 32, 64, 128}; N need not be a
  *             multiple of C.  The bf16 kernels run chunks of 32, 64 or 128
  *             tokens: an LA_BF16 request for C = 16 runs in 32-token chunks,
- *             which changes only the rounding.  B*H*N above 2^30 gives
- *             LA_ERR_UNSUPPORTED.
+ *             which changes only the rounding.  B*H*N above 2^30, or B*H
+ *             above 2^26, gives LA_ERR_UNSUPPORTED.
  *   q, k, v   [B][H][N][d] of dt, 16-byte aligned
  *   slope     [H] fp32, the decay is exp(-slope[h]); any finite slope >= 0
  *   state_in  [B][H][d][d] fp32, or NULL for a zero initial state

@@ -55,6 +55,9 @@ def test_prefill_validation():
     assert prefill(B=0) == SHAPE and prefill(H=0) == SHAPE and prefill(N=0) == SHAPE
     assert prefill(d=96) == SHAPE and prefill(dt=BF16, d=32) == SHAPE
     assert prefill(C=48) == SHAPE and prefill(C=256) == SHAPE
+    # size limits: B*H*N above 2^30, or B*H above 2^26 (int grid indexing)
+    assert prefill(B=1 << 12, H=1 << 10, N=1 << 9) == UNSUP
+    assert prefill(dt=F32, B=1 << 14, H=1 << 13, N=1, d=64) == UNSUP
     # bf16 C = 16 is accepted and runs 32-token chunks: same plan, same workspace
     assert prefill(dt=BF16, C=16) == WS
     assert la.workspace_bytes(0, BF16, 1, 2, 256, 128, 16) == la.workspace_bytes(0, BF16, 1, 2, 256, 128, 32)
