@@ -398,7 +398,7 @@ __global__ __launch_bounds__(D / 32 * 64) void bwd_kv_bf16_kernel(BwdPass p, con
           gh[ct][rd * (G::KSD / 2) + ks] = col_frag(Th, ks, lV[ct]);
           gl[ct][rd * (G::KSD / 2) + ks] = col_frag(Tl, ks, lV[ct]);
         }
-      if (rd == 0) lds_barrier();  // the half buffer is read before round 1 rewrites it
+      if (rd == 0) lds_barrier();  // the half buffer is read before the second half rewrites it
     }
     // dV = pass B's output (its q is K), with G^T from the exchange
     outputs(Kc, gh, gl, vfB, PBh, PBl, dvg, tc, n);
