@@ -779,7 +779,10 @@ la_status_t la_probe_stream_rmw(float* x, size_t n, float a, int load_policy, in
     if (load_policy != 0 && load_policy != la::kCpolNt) return LA_ERR_UNSUPPORTED;
     if (store_policy != 0 && store_policy != la::kCpolNt && store_policy != la::kCpolSc1)
       return LA_ERR_UNSUPPORTED;
-    if (n == 0 || n % 4 != 0 || n / 4 > (size_t)UINT32_MAX * 1024) return LA_ERR_BAD_SHAPE;
+    // one workgroup of 256 threads per 1024 float4: the launch's 32-bit count of
+    // work-items holds at most 2^24 - 1 workgroups
+    if (n == 0 || n % 4 != 0) return LA_ERR_BAD_SHAPE;
+    if (n / 4 > (size_t)((1u << 24) - 1) * 1024) return LA_ERR_UNSUPPORTED;
     if (!aligned16(x)) return LA_ERR_ALIGNMENT;
     return hip_status(
         la::launch_stream_rmw(x, n, a, load_policy, store_policy, (hipStream_t)stream));

@@ -375,7 +375,8 @@ size_t la_workspace_bytes_varlen(int op, la_dtype_t dt, int H, int d, int C,
  * arithmetic, so its rate is the HBM rate that access pattern can reach on
  * the GPU it runs on (the ceiling the decode step is compared with).
  *   x             device pointer, 16-byte aligned
- *   n             a positive multiple of 4
+ *   n             a positive multiple of 4, at most 4 * 1024 * (2^24 - 1)
+ *                 (LA_ERR_UNSUPPORTED above)
  *   load_policy   cache-policy bits of the loads: 0 or LA_CPOL_NT
  *   store_policy  of the stores: 0, LA_CPOL_NT or LA_CPOL_SC1
  *                 (the decode kernels use LA_CPOL_NT loads, LA_CPOL_SC1

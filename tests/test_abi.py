@@ -211,6 +211,7 @@ def test_probe_validation():
     f = la.lib().la_probe_stream_rmw
     assert f(None, 16, 1.0, 2, 16, None) == NULLP
     assert f(Q, 0, 1.0, 2, 16, None) == SHAPE and f(Q, 6, 1.0, 2, 16, None) == SHAPE
+    assert f(Q, 4 * 1024 * (1 << 24), 1.0, 2, 16, None) == UNSUP  # grid above 2^24 - 1
     assert f(Q + 8, 16, 1.0, 2, 16, None) == ALIGN
     assert f(Q, 16, 1.0, 1, 16, None) == UNSUP  # sc0 loads are not offered
     assert f(Q, 16, 1.0, 2, 18, None) == UNSUP  # nor nt|sc1 stores

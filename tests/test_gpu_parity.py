@@ -431,6 +431,22 @@ def test_decode_tokens(oracle_mod, dtype, B, H, K, d):
     assert_close(to_host(tS), rS, dtype, "S", stored_bf16=False)
 
 
+@pytest.mark.parametrize("load_policy,store_policy", [
+    (0, 0), (la.CPOL_NT, la.CPOL_NT), (la.CPOL_NT, la.CPOL_SC1)])
+def test_stream_probe_scales_in_place(load_policy, store_policy):
+    # the measurement helper the decode step is compared with: x <- a x over
+    # three full 1024-float4 workgroups and a ragged fourth, every element once
+    n = 4 * (3 * 1024 + 100)
+    g = torch.Generator(device="cpu").manual_seed(11)
+    x0 = torch.randn(n + 64, generator=g, dtype=torch.float32)
+    x = x0.to(device())
+    la.probe_stream_rmw(x[:n], a=2.0, load_policy=load_policy, store_policy=store_policy)
+    torch.cuda.synchronize()
+    got = x.cpu()
+    assert torch.equal(got[:n], 2.0 * x0[:n])
+    assert torch.equal(got[n:], x0[n:])  # nothing past n is touched
+
+
 def test_decode_tokens_equals_single_steps():
     """Against K calls of la_decode_step on the same inputs (bf16)."""
     B, H, K, d = 4, 8, 6, 128
