@@ -221,10 +221,11 @@ la_status_t scratch_address(void** out) {
 la_status_t check_seq(la_dtype_t dt, int B, int H, int N, int d, int C) {
   if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_BAD_DTYPE;
   if (B < 1 || H < 1 || N < 1 || !d_ok(dt, d) || !c_ok(C)) return LA_ERR_BAD_SHAPE;
-  // int indexing of grids and token offsets inside the kernels: token
-  // offsets below 2^30 and grids of at most 24 workgroups per row below 2^31
+  // int indexing of token offsets inside the kernels (below 2^30), and a
+  // launch's 32-bit count of work-items: at most 24 workgroups of 256
+  // threads per row (the fp32 short-row kernel), so B H rows below 2^19
   if ((long long)B * H * N > (1LL << 31) / 2) return LA_ERR_UNSUPPORTED;
-  if ((long long)B * H > (1LL << 26)) return LA_ERR_UNSUPPORTED;
+  if ((long long)B * H > (1LL << 19)) return LA_ERR_UNSUPPORTED;
   return LA_OK;
 }
 
@@ -421,7 +422,9 @@ la_status_t check_packed(la_dtype_t dt, int H, int d, int C, int nseq, const int
                          la::SeqTable* t, Plan* plan) {
   if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_BAD_DTYPE;
   if (H < 1 || nseq < 1 || !d_ok(dt, d) || !c_ok(C)) return LA_ERR_BAD_SHAPE;
-  if (nseq > la::kMaxSeqs) return LA_ERR_UNSUPPORTED;
+  // at most kMaxSeqs * H rows of 8 fp32 column slices of 256 threads: the
+  // launch's 32-bit count of work-items
+  if (nseq > la::kMaxSeqs || H > 4096) return LA_ERR_UNSUPPORTED;
   if (!cu) return LA_ERR_NULL_POINTER;
   if (cu[0] != 0) return LA_ERR_BAD_SHAPE;
   for (int s = 0; s < nseq; ++s)
@@ -629,7 +632,8 @@ la_status_t la_decode_step(la_dtype_t dt, int B, int H, int d, const void* q, co
   try {
     if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_BAD_DTYPE;
     if (B < 1 || H < 1 || !d_ok(dt, d)) return LA_ERR_BAD_SHAPE;
-    if ((long long)B * H > (1LL << 30)) return LA_ERR_UNSUPPORTED;  // grid of 2 B H workgroups
+    // 2 B H workgroups of 512 threads: the launch's 32-bit count of work-items
+    if ((long long)B * H > (1LL << 21)) return LA_ERR_UNSUPPORTED;
     if (!q || !k || !v || !slope || !state || !o) return LA_ERR_NULL_POINTER;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) ||
         !aligned16(o) || ((uintptr_t)slope & 3u))
@@ -655,7 +659,9 @@ la_status_t la_decode_tokens(la_dtype_t dt, int B, int H, int K, int d, const vo
     if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_BAD_DTYPE;
     if (B < 1 || H < 1 || K < 1 || !d_ok(dt, d)) return LA_ERR_BAD_SHAPE;
     if (K > 128) return LA_ERR_UNSUPPORTED;
+    // the limits of la_prefill, whose kernels serve K > 16
     if ((long long)B * H * K > (1LL << 31) / 2) return LA_ERR_UNSUPPORTED;
+    if ((long long)B * H > (1LL << 19)) return LA_ERR_UNSUPPORTED;
     if (!q || !k || !v || !slope || !state || !o) return LA_ERR_NULL_POINTER;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) ||
         !aligned16(o) || ((uintptr_t)slope & 3u))

@@ -85,7 +85,7 @@ typedef enum {
  *             multiple of C.  The bf16 kernels run chunks of 32, 64 or 128
  *             tokens: an LA_BF16 request for C = 16 runs in 32-token chunks,
  *             which changes only the rounding.  B*H*N above 2^30, or B*H
- *             above 2^26, gives LA_ERR_UNSUPPORTED.
+ *             above 2^19, gives LA_ERR_UNSUPPORTED.
  *   q, k, v   [B][H][N][d] of dt, 16-byte aligned
  *   slope     [H] fp32, the decay is exp(-slope[h]); any finite slope >= 0
  *   state_in  [B][H][d][d] fp32, or NULL for a zero initial state
@@ -202,7 +202,7 @@ la_status_t la_prefill_main(la_dtype_t dt, int B, int H, int N, int d, int C,
  * operation used for decoding ("Hybrid Linear Attention" section: O(n)
  * training and decoding).
  *
- *   B, H      >= 1, B*H at most 2^30 (LA_ERR_UNSUPPORTED above)
+ *   B, H      >= 1, B*H at most 2^21 (LA_ERR_UNSUPPORTED above)
  *   q, k, v   [B][H][d] of dt
  *   slope     [H] fp32
  *   state     [B][H][d][d] fp32, read and written in place: read with
@@ -226,7 +226,8 @@ la_status_t la_decode_step(la_dtype_t dt, int B, int H, int d, const void *q,
  * Either way the state is read and written once instead of K times.
  *
  *   dt        LA_F32 or LA_BF16;  B, H >= 1;  1 <= K <= 128 (more gives
- *             LA_ERR_UNSUPPORTED: use la_prefill with state_out = state_in)
+ *             LA_ERR_UNSUPPORTED: use la_prefill with state_out = state_in);
+ *             B*H at most 2^19, B*H*K at most 2^30 (LA_ERR_UNSUPPORTED above)
  *   d         as for la_prefill
  *   q, k, v   [B][H][K][d] of dt
  *   slope     [H] fp32
@@ -310,7 +311,7 @@ size_t la_workspace_bytes(int op, la_dtype_t dt, int B, int H, int N, int d,
  * sequence in two calls, the second with the first's state_out as state_in,
  * gives the result of one call over the whole sequence.
  *
- *   dt, d, C   as for la_prefill;  H >= 1
+ *   dt, d, C   as for la_prefill;  1 <= H <= 4096 (more gives LA_ERR_UNSUPPORTED)
  *   nseq       1 .. 256 (more gives LA_ERR_UNSUPPORTED)
  *   cu_seqlens HOST array of nseq + 1 ints, read during the call only:
  *              cu_seqlens[0] = 0, non-decreasing (empty sequences allowed);

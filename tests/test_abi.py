@@ -55,9 +55,9 @@ def test_prefill_validation():
     assert prefill(B=0) == SHAPE and prefill(H=0) == SHAPE and prefill(N=0) == SHAPE
     assert prefill(d=96) == SHAPE and prefill(dt=BF16, d=32) == SHAPE
     assert prefill(C=48) == SHAPE and prefill(C=256) == SHAPE
-    # size limits: B*H*N above 2^30, or B*H above 2^26 (int grid indexing)
+    # size limits: B*H*N above 2^30, or B*H above 2^19 (32-bit work-item counts)
     assert prefill(B=1 << 12, H=1 << 10, N=1 << 9) == UNSUP
-    assert prefill(dt=F32, B=1 << 14, H=1 << 13, N=1, d=64) == UNSUP
+    assert prefill(dt=F32, B=1 << 10, H=(1 << 9) + 1, N=1, d=64) == UNSUP
     # bf16 C = 16 is accepted and runs 32-token chunks: same plan, same workspace
     assert prefill(dt=BF16, C=16) == WS
     assert la.workspace_bytes(0, BF16, 1, 2, 256, 128, 16) == la.workspace_bytes(0, BF16, 1, 2, 256, 128, 32)
@@ -83,6 +83,7 @@ def test_decode_validation():
     assert call(st=None) == NULLP and call(k=None) == NULLP
     assert call(st=S_IN + 4) == ALIGN
     assert call(o=S_IN + 64) == ALIAS and call(st=Q) == ALIAS
+    assert call(B=1 << 11, H=(1 << 10) + 1) == UNSUP  # B*H above 2^21
 
 
 @pytest.mark.parametrize("entry", ["la_prefill_bwd", "la_prefill_bwd_reuse"])
@@ -129,6 +130,7 @@ def test_varlen_validation():
     assert call(cu=(1, 100)) == SHAPE  # must start at 0
     assert call(cu=(0, 100, 50)) == SHAPE  # must not decrease
     assert call(cu=tuple(range(258))) == UNSUP  # 257 sequences
+    assert call(H=4097) == UNSUP
     assert call(q=None) == NULLP and call(o=None) == NULLP
     assert call(q=Q + 8) == ALIGN and call(s_out=S_OUT + 4) == ALIGN
     assert call(o=K) == ALIAS and call(s_in=S_IN, s_out=S_IN + 16) == ALIAS
@@ -174,9 +176,11 @@ def test_decode_tokens_validation():
     assert call(dt=3) == DTYPE
     assert call(nk=0) == SHAPE and call(B=0) == SHAPE and call(d=100) == SHAPE
     assert call(nk=129) == UNSUP
+    assert call(B=1 << 10, H=(1 << 9) + 1, nk=1) == UNSUP  # B*H above 2^19
     assert call(st=None) == NULLP and call(q=None) == NULLP
     assert call(st=S_IN + 4) == ALIGN
     assert call(o=S_IN + 64) == ALIAS and call(st=Q) == ALIAS
+    assert call(B=1 << 11, H=(1 << 10) + 1) == UNSUP  # B*H above 2^21
 
 
 def test_gated_prefill_validation():
