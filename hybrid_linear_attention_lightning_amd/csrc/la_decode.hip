@@ -9,11 +9,10 @@
 // The d x d fp32 state dominates the traffic (2 * 4 * d^2 bytes per (b, h)
 // against 8 * d bytes of token data), so the kernel is a streaming
 // read-modify-write:
-//  * a workgroup owns a slice of at most 64 value columns of one (b, h)
-//    (o_t[j] = sum_i q_t[i] S_t[i][j] needs all rows of column j, so the
-//    columns split with no reduction between workgroups): 2 workgroups per
-//    (b, h) at d = 128, so that more, shorter workgroups overlap one
-//    another's reads and writes;
+//  * a workgroup owns one (b, h) (the columns could split across workgroups
+//    with no reduction between them, since o_t[j] = sum_i q_t[i] S_t[i][j]
+//    needs only column j, but measured one workgroup of 1024 threads per
+//    (b, h) is fastest, below);
 //  * each thread owns 4 adjacent value columns and every RG-th key row,
 //    issues all its 16-byte state loads before any arithmetic and writes the
 //    updated rows back with 16-byte stores;
@@ -31,6 +30,10 @@
 //    between a wave's state loads and its stores (measured 1% faster than
 //    staging the token in LDS first, with the state from HBM or not); with
 //    several tokens they are staged in LDS once for the workgroup.
+// On the B=64, H=32, d=128 step (one machine, best of three rounds), state
+// from HBM / state in the Infinity Cache: 1024 threads per (b, h) 45.0 /
+// 39.2 us; 512 threads per (b, h) 45.1 / 39.7 us; 1024 threads per half of
+// the columns 44.2 / 41.6 us; 512 threads per half 47.2 / 41.0 us.
 #include "la_common.h"
 #include "la_internal.h"
 
@@ -56,23 +59,24 @@ __device__ __forceinline__ void st_state(__amdgpu_buffer_rsrc_t r, uint32_t off,
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, kCpolSc1);
 }
 
-// Value columns per workgroup.
+// Value columns per workgroup: all of them.
 template <int D>
-constexpr int decode_cols() { return D < 64 ? D : 64; }
+constexpr int decode_cols() { return D; }
+// Threads per workgroup: one per (4 columns, row) up to 1024.
+template <int D>
+constexpr int dec_threads() { return D / 4 * D < 1024 ? D / 4 * D : 1024; }
 
 // K tokens (1 <= K <= KMAX) per (b, h): token j updates the state and reads
 // o_j = q_j^T S_j, the K steps of the recurrence on a state held in
 // registers, so the state is streamed once for all K tokens.  Workgroup
 // (b h) * SPLIT + part owns value columns part * COLS .. +COLS-1.
-// Threads per workgroup: 512 (8 waves) measured 1% faster than 256 and 4%
-// faster than 128 on the B=64, H=32, d=128 step with the state from HBM.
-constexpr int kDecThreads = 512;
 template <int D, typename T, int KMAX>
-__global__ __launch_bounds__(kDecThreads) void decode_kernel(int H, int K, const T* __restrict__ q,
+__global__ __launch_bounds__(dec_threads<D>()) void decode_kernel(int H, int K, const T* __restrict__ q,
                                                     const T* __restrict__ k,
                                                     const T* __restrict__ v,
                                                     const float* __restrict__ slope,
                                                     float* __restrict__ state, T* __restrict__ o) {
+  constexpr int kDecThreads = dec_threads<D>();
   constexpr int COLS = decode_cols<D>();
   constexpr int SPLIT = D / COLS;  // workgroups per (b, h)
   constexpr int CG = COLS / 4;     // float4 column groups
@@ -91,7 +95,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(int H, int K, const
   float* Sw = state + (size_t)bh * D * D + c_base;  // the workgroup's slice
   float* S = Sw + 4 * cg;
 
-  const bool active = tid < CG * RG;  // every thread unless d < 64
+  const bool active = tid < CG * RG;  // every thread: the workgroup has CG * RG
 
   // issue the state loads first: they are the whole cost
   f32x4_t sv[ROWS];
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(int H, int K, const
 template <int D, int KMAX>
 hipError_t launch_d(bool bf16, int B, int H, int K, const void* q, const void* k, const void* v,
                     const float* slope, float* state, void* o, hipStream_t s) {
-  const dim3 grid((unsigned)(B * H * (D / decode_cols<D>()))), block(kDecThreads);
+  const dim3 grid((unsigned)(B * H * (D / decode_cols<D>()))), block(dec_threads<D>());
   if (bf16)
     hipLaunchKernelGGL((decode_kernel<D, uint16_t, KMAX>), grid, block, 0, s, H, K,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, slope, state,
