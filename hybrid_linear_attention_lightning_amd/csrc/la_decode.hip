@@ -83,7 +83,7 @@ __global__ __launch_bounds__(dec_threads<D>()) void decode_kernel(int H, int K, 
   constexpr int RG = (kDecThreads / CG < D) ? kDecThreads / CG : D;  // row groups
   constexpr int ROWS = D / RG;     // rows per thread
   constexpr int NWV = (CG * RG + 63) / 64;           // active waves
-  __shared__ float qs[KMAX][D], ks[KMAX][D], vs[KMAX][COLS];
+  __shared__ __attribute__((aligned(16))) float qs[KMAX][D], ks[KMAX][D], vs[KMAX][COLS];
   __shared__ f32x4_t red[KMAX][NWV][CG];
 
   const int bh = blockIdx.x / SPLIT;
@@ -139,10 +139,13 @@ __global__ __launch_bounds__(dec_threads<D>()) void decode_kernel(int H, int K, 
       if (lane < CG) red[0][wv][cg] = acc;
     }
   } else {
+  // q and k entries stored by row group: row rg + RG m at rg ROWS + m, so
+  // that a thread reads its ROWS entries of a token as one vector
   for (int e = tid; e < K * D; e += kDecThreads) {
     const int j = e / D, c = e - j * D;
-    qs[j][c] = ld_tok(q + tok0, e);
-    ks[j][c] = ld_tok(k + tok0, e);
+    const int x = (c % RG) * ROWS + c / RG;
+    qs[j][x] = ld_tok(q + tok0, e);
+    ks[j][x] = ld_tok(k + tok0, e);
   }
   for (int e = tid; e < K * COLS; e += kDecThreads) {
     const int j = e / COLS, c = e - j * COLS;
@@ -156,8 +159,7 @@ __global__ __launch_bounds__(dec_threads<D>()) void decode_kernel(int H, int K, 
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < ROWS; ++m) {
-        const int i = rg + RG * m;
-        const float ki = ks[j][i], qi = qs[j][i];
+        const float ki = ks[j][ROWS * rg + m], qi = qs[j][ROWS * rg + m];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           sv[m][c] = fmaf(lam, sv[m][c], ki * v4[c]);
