@@ -254,7 +254,8 @@ def bench_tiny_f32(args, torch, la, la_inputs):
             "us_per_call": us, "tokens_per_s": B * N / (us * 1e-6),
             "us_per_call_graph": us_graph, "calls_per_graph": n, "replays": reps,
             "note": "fwd_f32_quad_kernel: rows of at most 256 tokens in the parallel form, one "
-                    "workgroup per 16 query rows and per 16 state rows (40 here); us_per_call: "
+                    "workgroup (two 256-thread halves taking alternate key steps) per 16 query "
+                    "rows and per 16 state rows (40 here); us_per_call: "
                     "calls back to back from Python, us_per_call_graph: the same call replayed "
                     "from a HIP graph (null if a replay differed from the eager result)"}
 

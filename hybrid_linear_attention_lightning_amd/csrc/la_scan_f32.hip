@@ -318,22 +318,31 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdPass p, const SeqTable 
 // a few chunk latencies on a nearly idle GPU; here every block of QB query
 // rows and every block of QB state rows is its own workgroup, and the
 // longest dependency chain is one query block's pass over the keys in steps
-// of KB.  Its work grows as N^2, so it serves rows of at most kQuadMaxN
-// tokens.  Grid: rows x (ceil(N / QB) query blocks + D / QB state blocks
-// when the state is written).
+// of KB.  At d <= 64 a workgroup is two halves of 256 threads that take the
+// steps alternately, each with its own K, V and score buffers, and add their
+// partial sums in a fixed order at the end (the chain is half as long, the
+// result stays bitwise reproducible); at d = 128 the buffers of a second
+// half do not fit the LDS beside S0, and one half takes every step.  Its
+// work grows as N^2, so it serves rows of at most kQuadMaxN tokens.  Grid:
+// rows x (ceil(N / QB) query blocks + D / QB state blocks when the state is
+// written).
 constexpr int kQuadQB = 16, kQuadKB = 64;
 template <int D>
-__global__ __launch_bounds__(256) void fwd_f32_quad_kernel(FwdPass p, int nqb, int nblk) {
-  constexpr int QB = kQuadQB, KB = kQuadKB;
+constexpr int quad_halves() { return D <= 64 ? 2 : 1; }
+template <int D>
+__global__ __launch_bounds__(256 * quad_halves<D>()) void fwd_f32_quad_kernel(FwdPass p, int nqb,
+                                                                             int nblk) {
+  constexpr int QB = kQuadQB, KB = kQuadKB, NH = quad_halves<D>();
   constexpr int DP = D + 4;       // padded rows of Q, K, V and S0
   constexpr int CG = D / 4;       // float4 column groups of a row
   constexpr int PAIRS = QB * CG;  // (row, column group) outputs of a block
-  constexpr int NP = (PAIRS + 255) / 256;  // of them per thread
+  constexpr int NP = (PAIRS + 255) / 256;  // of them per thread of a half
   constexpr int TV = KB * CG / 256;        // float4 of a KB-row tile per thread
   static_assert(D % 16 == 0 && TV >= 1, "head dim");
-  __shared__ __attribute__((aligned(16))) float Qs[QB * DP], Ks[KB * DP], Vs[KB * DP],
-      Ps[QB * (KB + 4)], bt[KB], Ss[D * DP];
-  const int tid = threadIdx.x;
+  // per half: K, V (or, for state blocks, K columns as [KB][QB]), scores, b
+  __shared__ __attribute__((aligned(16))) float Qs[QB * DP], Ks[NH][KB * DP], Vs[NH][KB * DP],
+      Ps[NH][QB * (KB + 4)], bt[NH][KB], Ss[D * DP];
+  const int hf = threadIdx.x / 256, tid = threadIdx.x % 256;  // half, thread in the half
   const int r_idx = blockIdx.x / nblk, blk = blockIdx.x % nblk;
   const int N = p.N, h = r_idx % p.H;
   const float sl2 = p.slope[h] * kLog2e;
@@ -344,6 +353,7 @@ __global__ __launch_bounds__(256) void fwd_f32_quad_kernel(FwdPass p, int nqb, i
   const float* S0 = p.state_in ? p.state_in + (size_t)r_idx * D * D : nullptr;
   // rows r0 .. r0 + KB - 1 of a token tensor (zero past N), TV float4 per
   // thread: fetched into registers one step ahead, then put into LDS
+  f32x4_t kr[TV], vr[TV];
   auto fetch = [&](f32x4_t (&x)[TV], const float* src, int r0) {
 #pragma unroll
     for (int u = 0; u < TV; ++u) {
@@ -359,88 +369,106 @@ __global__ __launch_bounds__(256) void fwd_f32_quad_kernel(FwdPass p, int nqb, i
       *reinterpret_cast<f32x4_t*>(dst + (e / CG) * DP + 4 * (e % CG)) = x[u];
     }
   };
-  f32x4_t kr[TV], vr[TV];
+  // the halves' partial sums meet in half 0 through half 1's K buffer
+  float* part = Ks[NH - 1];
+  f32x4_t acc[NP];
+#pragma unroll
+  for (int u = 0; u < NP; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   if (blk < nqb) {
     // ---- query rows i0 .. i0 + QB - 1 -------------------------------------
     const int i0 = QB * blk;
     const int kend = min(N, i0 + QB);  // keys 0 .. kend - 1 reach the block
-    fetch(kr, kg, 0);
-    fetch(vr, vg, 0);
-    for (int e = tid; e < QB * CG; e += 256) {
+    const int nsteps = (kend + KB - 1) / KB;
+    if (hf < nsteps) {
+      fetch(kr, kg, KB * hf);
+      fetch(vr, vg, KB * hf);
+    }
+    for (int e = threadIdx.x; e < QB * CG; e += 256 * NH) {
       const int r = e / CG, c4 = e % CG;
       f32x4_t x = {0.f, 0.f, 0.f, 0.f};
       if (i0 + r < N) x = *reinterpret_cast<const f32x4_t*>(qg + (size_t)(i0 + r) * D + 4 * c4);
       *reinterpret_cast<f32x4_t*>(Qs + r * DP + 4 * c4) = x;
     }
     if (S0) {
-      for (int e = tid; e < D * CG; e += 256) {
+      for (int e = threadIdx.x; e < D * CG; e += 256 * NH) {
         const int r = e / CG, c4 = e % CG;
         *reinterpret_cast<f32x4_t*>(Ss + r * DP + 4 * c4) =
             *reinterpret_cast<const f32x4_t*>(S0 + (size_t)r * D + 4 * c4);
       }
     }
-    f32x4_t acc[NP];
-#pragma unroll
-    for (int u = 0; u < NP; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // score entries of this thread: query row i0 + si, keys sj + 16 m
     const int si = tid / 16, sj = tid % 16;
-    for (int j0 = 0; j0 < kend; j0 += KB) {
-      __syncthreads();  // the previous step is done with Ks, Vs and Ps
-      put(Ks, kr);
-      put(Vs, vr);
-      if (j0 + KB < kend) {  // the next step's keys load during this one
-        fetch(kr, kg, j0 + KB);
-        fetch(vr, vg, j0 + KB);
-      }
-      __syncthreads();
-      // masked, decayed scores P[si][sj + 16 m]
-      float sc[KB / 16];
-#pragma unroll
-      for (int m = 0; m < KB / 16; ++m) sc[m] = 0.f;
-#pragma unroll 4
-      for (int f = 0; f < D; f += 4) {
-        const f32x4_t qa = *reinterpret_cast<const f32x4_t*>(Qs + si * DP + f);
-#pragma unroll
-        for (int m = 0; m < KB / 16; ++m) {
-          const f32x4_t kb = *reinterpret_cast<const f32x4_t*>(Ks + (sj + 16 * m) * DP + f);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sc[m] = fmaf(qa[e], kb[e], sc[m]);
+    float* Kh = Ks[hf];
+    float* Vh = Vs[hf];
+    float* Ph = Ps[hf];
+    // every thread runs the same number of rounds (barriers); in round it,
+    // half hf takes step NH it + hf when it exists
+    for (int it = 0; it * NH < nsteps; ++it) {
+      const int st = NH * it + hf;
+      const bool mine = st < nsteps;
+      const int j0 = KB * st;
+      __syncthreads();  // the previous round is done with this half's buffers
+      if (mine) {
+        put(Kh, kr);
+        put(Vh, vr);
+        if (st + NH < nsteps) {  // this half's next step loads during this one
+          fetch(kr, kg, j0 + KB * NH);
+          fetch(vr, vg, j0 + KB * NH);
         }
       }
+      __syncthreads();
+      if (mine) {
+        // masked, decayed scores P[si][sj + 16 m]
+        float sc[KB / 16];
 #pragma unroll
-      for (int m = 0; m < KB / 16; ++m) {
-        const int i = i0 + si, j = j0 + sj + 16 * m;
-        Ps[si * (KB + 4) + sj + 16 * m] = j <= i ? sc[m] * exp2f(-sl2 * (float)(i - j)) : 0.f;
+        for (int m = 0; m < KB / 16; ++m) sc[m] = 0.f;
+#pragma unroll 4
+        for (int f = 0; f < D; f += 4) {
+          const f32x4_t qa = *reinterpret_cast<const f32x4_t*>(Qs + si * DP + f);
+#pragma unroll
+          for (int m = 0; m < KB / 16; ++m) {
+            const f32x4_t kb = *reinterpret_cast<const f32x4_t*>(Kh + (sj + 16 * m) * DP + f);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc[m] = fmaf(qa[e], kb[e], sc[m]);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < KB / 16; ++m) {
+          const int i = i0 + si, j = j0 + sj + 16 * m;
+          Ph[si * (KB + 4) + sj + 16 * m] = j <= i ? sc[m] * exp2f(-sl2 * (float)(i - j)) : 0.f;
+        }
       }
       __syncthreads();
-      // o[i][4 cg ..] += sum_j P[i][j] V[j][4 cg ..]
+      if (mine) {
+        // o[i][4 cg ..] += sum_j P[i][j] V[j][4 cg ..]
 #pragma unroll
-      for (int u = 0; u < NP; ++u) {
-        const int e = tid + 256 * u;
-        if (e < PAIRS) {
-          const int i = e / CG, cg = e % CG;
+        for (int u = 0; u < NP; ++u) {
+          const int e = tid + 256 * u;
+          if (e < PAIRS) {
+            const int i = e / CG, cg = e % CG;
 #pragma unroll 4
-          for (int j = 0; j < KB; j += 4) {
-            const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(Ps + i * (KB + 4) + j);
+            for (int j = 0; j < KB; j += 4) {
+              const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(Ph + i * (KB + 4) + j);
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              const f32x4_t vv = *reinterpret_cast<const f32x4_t*>(Vs + (j + x) * DP + 4 * cg);
+              for (int x = 0; x < 4; ++x) {
+                const f32x4_t vv = *reinterpret_cast<const f32x4_t*>(Vh + (j + x) * DP + 4 * cg);
 #pragma unroll
-              for (int c = 0; c < 4; ++c) acc[u][c] = fmaf(pr[x], vv[c], acc[u][c]);
+                for (int c = 0; c < 4; ++c) acc[u][c] = fmaf(pr[x], vv[c], acc[u][c]);
+              }
             }
           }
         }
       }
     }
-    // + lambda^(i+1) q_i^T S0 (S0 in LDS since the first step), then store
+    // + lambda^(i+1) q_i^T S0 (S0 in LDS since the first round), by the last
+    // half; then the halves' sums are added in half 0 and stored
+    if (S0 && hf == NH - 1) {
 #pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const int e = tid + 256 * u;
-      if (e >= PAIRS) continue;
-      const int i = e / CG, cg = e % CG;
-      if (i0 + i >= N) continue;
-      if (S0) {
+      for (int u = 0; u < NP; ++u) {
+        const int e = tid + 256 * u;
+        if (e >= PAIRS) continue;
+        const int i = e / CG, cg = e % CG;
         f32x4_t x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
         for (int f = 0; f < D; f += 4) {
@@ -456,11 +484,36 @@ __global__ __launch_bounds__(256) void fwd_f32_quad_kernel(FwdPass p, int nqb, i
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[u][c] = fmaf(a, x[c], acc[u][c]);
       }
-      *reinterpret_cast<f32x4_t*>((float*)p.o + head_off + (size_t)(i0 + i) * D + 4 * cg) = acc[u];
+    }
+    if constexpr (NH == 2) {
+      __syncthreads();  // every half is done with its buffers
+      if (hf == 1) {
+#pragma unroll
+        for (int u = 0; u < NP; ++u)
+          *reinterpret_cast<f32x4_t*>(part + 4 * (tid + 256 * u)) = acc[u];
+      }
+      __syncthreads();
+    }
+    if (hf == 0) {
+#pragma unroll
+      for (int u = 0; u < NP; ++u) {
+        const int e = tid + 256 * u;
+        if (e >= PAIRS) continue;
+        const int i = e / CG, cg = e % CG;
+        if (i0 + i >= N) continue;
+        f32x4_t y = acc[u];
+        if constexpr (NH == 2) {
+          const f32x4_t o1 = *reinterpret_cast<const f32x4_t*>(part + 4 * e);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) y[c] += o1[c];
+        }
+        *reinterpret_cast<f32x4_t*>((float*)p.o + head_off + (size_t)(i0 + i) * D + 4 * cg) = y;
+      }
     }
   } else {
     // ---- state rows f0 .. f0 + QB - 1 of S_N ------------------------------
     const int f0 = QB * (blk - nqb);
+    const int nsteps = (N + KB - 1) / KB;
     // K columns f0 .. f0 + QB - 1 of KB tokens: one float4 per thread
     static_assert(KB * (QB / 4) == 256, "one K float4 per thread");
     const int kr_r = tid / (QB / 4), kr_c = tid % (QB / 4);
@@ -470,52 +523,82 @@ __global__ __launch_bounds__(256) void fwd_f32_quad_kernel(FwdPass p, int nqb, i
         x = *reinterpret_cast<const f32x4_t*>(kg + (size_t)(t0 + kr_r) * D + f0 + 4 * kr_c);
       return x;
     };
-    f32x4_t kc = fetch_k(0);
-    fetch(vr, vg, 0);
-    f32x4_t acc[NP];
-    const float gN = exp2f(-sl2 * (float)N);
-#pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const int e = tid + 256 * u;
-      acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if (S0 && e < PAIRS) {
-        const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(S0 + (size_t)(f0 + e / CG) * D +
-                                                             4 * (e % CG));
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[u][c] = gN * s0[c];
-      }
+    f32x4_t kc = {0.f, 0.f, 0.f, 0.f};
+    if (hf < nsteps) {
+      kc = fetch_k(KB * hf);
+      fetch(vr, vg, KB * hf);
     }
-    for (int t0 = 0; t0 < N; t0 += KB) {
-      __syncthreads();  // the previous step is done with Ks, Vs and bt
-      *reinterpret_cast<f32x4_t*>(Ks + kr_r * QB + 4 * kr_c) = kc;  // Ks as [KB][QB]
-      put(Vs, vr);
-      if (tid < KB) bt[tid] = t0 + tid < N ? exp2f(-sl2 * (float)(N - 1 - t0 - tid)) : 0.f;
-      if (t0 + KB < N) {
-        kc = fetch_k(t0 + KB);
-        fetch(vr, vg, t0 + KB);
-      }
-      __syncthreads();
+    if (S0 && hf == 0) {
+      const float gN = exp2f(-sl2 * (float)N);
 #pragma unroll
       for (int u = 0; u < NP; ++u) {
         const int e = tid + 256 * u;
         if (e < PAIRS) {
-          const int fl = e / CG, cg = e % CG;
-#pragma unroll 8
-          for (int t = 0; t < KB; ++t) {
-            const float w = bt[t] * Ks[t * QB + fl];
-            const f32x4_t vv = *reinterpret_cast<const f32x4_t*>(Vs + t * DP + 4 * cg);
+          const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(S0 + (size_t)(f0 + e / CG) * D +
+                                                               4 * (e % CG));
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[u][c] = fmaf(w, vv[c], acc[u][c]);
+          for (int c = 0; c < 4; ++c) acc[u][c] = gN * s0[c];
+        }
+      }
+    }
+    float* Kh = Ks[hf];
+    float* Vh = Vs[hf];
+    float* bh = bt[hf];
+    for (int it = 0; it * NH < nsteps; ++it) {
+      const int st = NH * it + hf;
+      const bool mine = st < nsteps;
+      const int t0 = KB * st;
+      __syncthreads();  // the previous round is done with this half's buffers
+      if (mine) {
+        *reinterpret_cast<f32x4_t*>(Kh + kr_r * QB + 4 * kr_c) = kc;  // Kh as [KB][QB]
+        put(Vh, vr);
+        if (tid < KB) bh[tid] = t0 + tid < N ? exp2f(-sl2 * (float)(N - 1 - t0 - tid)) : 0.f;
+        if (st + NH < nsteps) {
+          kc = fetch_k(t0 + KB * NH);
+          fetch(vr, vg, t0 + KB * NH);
+        }
+      }
+      __syncthreads();
+      if (mine) {
+#pragma unroll
+        for (int u = 0; u < NP; ++u) {
+          const int e = tid + 256 * u;
+          if (e < PAIRS) {
+            const int fl = e / CG, cg = e % CG;
+#pragma unroll 8
+            for (int t = 0; t < KB; ++t) {
+              const float w = bh[t] * Kh[t * QB + fl];
+              const f32x4_t vv = *reinterpret_cast<const f32x4_t*>(Vh + t * DP + 4 * cg);
+#pragma unroll
+              for (int c = 0; c < 4; ++c) acc[u][c] = fmaf(w, vv[c], acc[u][c]);
+            }
           }
         }
       }
     }
+    if constexpr (NH == 2) {
+      __syncthreads();
+      if (hf == 1) {
 #pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const int e = tid + 256 * u;
-      if (e < PAIRS)
+        for (int u = 0; u < NP; ++u)
+          *reinterpret_cast<f32x4_t*>(part + 4 * (tid + 256 * u)) = acc[u];
+      }
+      __syncthreads();
+    }
+    if (hf == 0) {
+#pragma unroll
+      for (int u = 0; u < NP; ++u) {
+        const int e = tid + 256 * u;
+        if (e >= PAIRS) continue;
+        f32x4_t y = acc[u];
+        if constexpr (NH == 2) {
+          const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(part + 4 * e);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) y[c] += s1[c];
+        }
         *reinterpret_cast<f32x4_t*>(p.state_out + (size_t)r_idx * D * D +
-                                    (size_t)(f0 + e / CG) * D + 4 * (e % CG)) = acc[u];
+                                    (size_t)(f0 + e / CG) * D + 4 * (e % CG)) = y;
+      }
     }
   }
 }
@@ -525,7 +608,8 @@ hipError_t launch_f32_quad(const FwdPass& p, hipStream_t s) {
   const int nqb = (p.N + kQuadQB - 1) / kQuadQB;
   const int nblk = nqb + (p.state_out ? D / kQuadQB : 0);
   const unsigned grid = (unsigned)(p.B * p.H * nblk);
-  hipLaunchKernelGGL((fwd_f32_quad_kernel<D>), dim3(grid), dim3(256), 0, s, p, nqb, nblk);
+  hipLaunchKernelGGL((fwd_f32_quad_kernel<D>), dim3(grid), dim3(256 * quad_halves<D>()), 0, s, p,
+                     nqb, nblk);
   return hipGetLastError();
 }
 
