@@ -632,7 +632,7 @@ la_status_t la_decode_step(la_dtype_t dt, int B, int H, int d, const void* q, co
   try {
     if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_BAD_DTYPE;
     if (B < 1 || H < 1 || !d_ok(dt, d)) return LA_ERR_BAD_SHAPE;
-    // 2 B H workgroups of 512 threads: the launch's 32-bit count of work-items
+    // B H workgroups of at most 1024 threads: the launch's 32-bit count of work-items
     if ((long long)B * H > (1LL << 21)) return LA_ERR_UNSUPPORTED;
     if (!q || !k || !v || !slope || !state || !o) return LA_ERR_NULL_POINTER;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) ||
