@@ -29,7 +29,10 @@
 //    rows and the v entries of its columns itself, so no barrier stands
 //    between a wave's state loads and its stores (measured 1% faster than
 //    staging the token in LDS first, with the state from HBM or not); with
-//    several tokens they are staged in LDS once for the workgroup.
+//    several tokens they are staged in LDS once for the workgroup, and the
+//    wave partials of o go through LDS in rounds of at most 8 tokens (4
+//    above 8), so that two workgroups still fit on a CU at 16 tokens
+//    (16-token call 82 against 101 us with all 16 partials at once).
 // On the B=64, H=32, d=128 step (one machine, best of three rounds), state
 // from HBM / state in the Infinity Cache: 1024 threads per (b, h) 45.0 /
 // 39.2 us; 512 threads per (b, h) 45.1 / 39.7 us; 1024 threads per half of
@@ -84,7 +87,11 @@ __global__ __launch_bounds__(dec_threads<D>()) void decode_kernel(int H, int K, 
   constexpr int ROWS = D / RG;     // rows per thread
   constexpr int NWV = (CG * RG + 63) / 64;           // active waves
   __shared__ __attribute__((aligned(16))) float qs[KMAX][D], ks[KMAX][D], vs[KMAX][COLS];
-  __shared__ f32x4_t red[KMAX][NWV][CG];
+  // cross-wave partial sums of o, for up to KR tokens at a time: rounds of
+  // 4 tokens above 8 keep the workgroup's LDS below half of the CU's, so
+  // that two workgroups of 1024 threads still fit
+  constexpr int KR = KMAX <= 8 ? KMAX : 4;
+  __shared__ f32x4_t red[KR][NWV][CG];
 
   const int bh = blockIdx.x / SPLIT;
   const int c_base = (blockIdx.x % SPLIT) * COLS;  // first value column
@@ -105,6 +112,27 @@ __global__ __launch_bounds__(dec_threads<D>()) void decode_kernel(int H, int K, 
   }
 
   const size_t tok0 = (size_t)bh * K * D;
+  // o for tokens j0 .. j0 + nk - 1 from the waves' partials in red
+  auto reduce_store = [&](int j0, int nk) {
+    for (int e = tid; e < nk * CG; e += kDecThreads) {
+      const int j = e / CG, c4 = e - j * CG;
+      f32x4_t t = red[j][0][c4];
+#pragma unroll
+      for (int g = 1; g < NWV; ++g) {
+        const f32x4_t u = red[j][g][c4];
+        t[0] += u[0];
+        t[1] += u[1];
+        t[2] += u[2];
+        t[3] += u[3];
+      }
+      T* ob = o + tok0 + (size_t)(j0 + j) * D + c_base + 4 * c4;
+      if constexpr (sizeof(T) == 4) {
+        *reinterpret_cast<f32x4_t*>(ob) = t;
+      } else {
+        *reinterpret_cast<u32x2_t*>(ob) = u32x2_t{pack2(t[0], t[1]), pack2(t[2], t[3])};
+      }
+    }
+  };
   const float lam = expf(-slope[h]);
   if constexpr (KMAX == 1) {
     // one token: each thread loads the q and k entries of its rows and the v
@@ -153,8 +181,13 @@ __global__ __launch_bounds__(dec_threads<D>()) void decode_kernel(int H, int K, 
   }
   __syncthreads();
 
+  // tokens in rounds of KR; a round's partials are reduced before the next
+  // round writes its own (all but the last round end in two barriers, after
+  // the state loads have all been waited for)
+  for (int j0 = 0; j0 < K; j0 += KR) {
+  const int nk = K - j0 < KR ? K - j0 : KR;
   if (active) {
-    for (int j = 0; j < K; ++j) {
+    for (int j = j0; j < j0 + nk; ++j) {
       const f32x4_t v4 = {vs[j][4 * cg], vs[j][4 * cg + 1], vs[j][4 * cg + 2], vs[j][4 * cg + 3]};
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -172,33 +205,25 @@ __global__ __launch_bounds__(dec_threads<D>()) void decode_kernel(int H, int K, 
       for (int off = CG; off < 64; off <<= 1)
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
-      if (lane < CG) red[j][wv][cg] = acc;
+      if (lane < CG) red[j - j0][wv][cg] = acc;
     }
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(Sw);
+    if (j0 + nk == K) {
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(Sw);
 #pragma unroll
-    for (int m = 0; m < ROWS; ++m)
-      st_state(rs, (uint32_t)(((rg + RG * m) * D + 4 * cg) * sizeof(float)), sv[m]);
+      for (int m = 0; m < ROWS; ++m)
+        st_state(rs, (uint32_t)(((rg + RG * m) * D + 4 * cg) * sizeof(float)), sv[m]);
+    }
+  }
+  if (j0 + nk < K) {
+    __syncthreads();
+    reduce_store(j0, nk);
+    __syncthreads();
+  }
   }
   }
   __syncthreads();
-  for (int e = tid; e < K * CG; e += kDecThreads) {
-    const int j = e / CG, c4 = e - j * CG;
-    f32x4_t t = red[j][0][c4];
-#pragma unroll
-    for (int g = 1; g < NWV; ++g) {
-      const f32x4_t u = red[j][g][c4];
-      t[0] += u[0];
-      t[1] += u[1];
-      t[2] += u[2];
-      t[3] += u[3];
-    }
-    T* ob = o + tok0 + (size_t)j * D + c_base + 4 * c4;
-    if constexpr (sizeof(T) == 4) {
-      *reinterpret_cast<f32x4_t*>(ob) = t;
-    } else {
-      *reinterpret_cast<u32x2_t*>(ob) = u32x2_t{pack2(t[0], t[1]), pack2(t[2], t[3])};
-    }
-  }
+  const int last = KMAX == 1 ? 0 : (K - 1) / KR * KR;  // the last round's first token
+  reduce_store(last, K - last);
 }
 
 template <int D, int KMAX>

@@ -406,6 +406,8 @@ DECODE_TOKENS_CASES = [
     ("bf16", 2, 3, 4, 128),
     ("bf16", 2, 3, 8, 64),
     ("bf16", 2, 3, 16, 128),  # largest K of the streaming kernel
+    ("bf16", 2, 3, 13, 128),  # o reduced in rounds of 4 tokens, the last one short
+    ("f32", 2, 2, 9, 32),
     ("bf16", 2, 2, 17, 64),  # smallest K of the chunk path
     ("bf16", 2, 2, 33, 64),
     ("f32", 3, 2, 7, 16),
