@@ -42,6 +42,15 @@ struct Plan {
   size_t pieces_bytes = 0, seg_bytes = 0;
   size_t ws() const { return prepass ? pieces_bytes + seg_bytes + la::kTagBytes : 0; }
   size_t tag_off() const { return pieces_bytes + seg_bytes; }
+  // The piece kernel runs one workgroup of 2 d threads per piece state: the
+  // launch's 32-bit count of work-items bounds the number of pieces (a
+  // segment of a prime number of chunks has one-chunk pieces, so the size
+  // limits on B, H and N alone do not).
+  bool pieces_fit(int d) const {
+    if (!prepass) return true;
+    const unsigned long long slots = pieces_bytes / ((size_t)d * d * sizeof(float));
+    return slots * (2ull * d) < (1ull << 32);
+  }
 };
 
 // The chunk length the kernels run: the bf16 kernels take chunks of 32, 64
@@ -412,6 +421,7 @@ la_status_t check_prefill(la_dtype_t dt, int B, int H, int N, int d, int C, cons
     return LA_ERR_ALIAS;
   *plan = make_plan(dt, B, H, N, d, C);
   if (own_workspace) return LA_OK;  // the caller of check_prefill provides it
+  if (!plan->pieces_fit(d)) return LA_ERR_UNSUPPORTED;
   if (plan->ws() > 0 && (!workspace || workspace_bytes < plan->ws())) return LA_ERR_WORKSPACE;
   if (plan->ws() > 0 && !aligned16(workspace)) return LA_ERR_ALIGNMENT;
   return LA_OK;
@@ -431,6 +441,7 @@ la_status_t check_packed(la_dtype_t dt, int H, int d, int C, int nseq, const int
     if (cu[s + 1] < cu[s]) return LA_ERR_BAD_SHAPE;
   if ((long long)H * cu[nseq] > (1LL << 31) / 2) return LA_ERR_UNSUPPORTED;
   *plan = make_plan_packed(dt, H, d, C, nseq, cu, t);
+  if (!plan->pieces_fit(d)) return LA_ERR_UNSUPPORTED;
   return LA_OK;
 }
 
@@ -466,6 +477,7 @@ la_status_t prefill_bwd(la_dtype_t dt, int B, int H, int N, int d, int C, const 
         if (overlap(outs[a], tb, outs[b], tb)) return LA_ERR_ALIAS;
     }
     const Plan pl = make_plan(dt, B, H, N, d, C);
+    if (!pl.pieces_fit(d)) return LA_ERR_UNSUPPORTED;
     if (pl.ws() > 0 && (!workspace || workspace_bytes < pl.ws())) return LA_ERR_WORKSPACE;
     if (pl.ws() > 0 && !aligned16(workspace)) return LA_ERR_ALIGNMENT;
     return run_bwd(dt, pl, uniform_table(), B, H, N, d, C, q, k, v, dout, slope, dq, dk, dv,
@@ -542,6 +554,7 @@ la_status_t la_prefill_noalloc(la_dtype_t dt, int B, int H, int N, int d, int C,
                                    nullptr, 0, true, &pl, true);
     if (st != LA_OK) return st;
     if (!fit_plan(&pl, (long long)B * H, d, C, kScratchBytes)) return LA_ERR_WORKSPACE;
+    if (!pl.pieces_fit(d)) return LA_ERR_UNSUPPORTED;
     void* ws = nullptr;
     if (pl.ws() > 0) {
       st = scratch_address(&ws);

@@ -85,7 +85,11 @@ typedef enum {
  *             multiple of C.  The bf16 kernels run chunks of 32, 64 or 128
  *             tokens: an LA_BF16 request for C = 16 runs in 32-token chunks,
  *             which changes only the rounding.  B*H*N above 2^30, or B*H
- *             above 2^19, gives LA_ERR_UNSUPPORTED.
+ *             above 2^19, gives LA_ERR_UNSUPPORTED, and so does a segment
+ *             plan whose pieces would need more than 2^32 work-items (one
+ *             workgroup of 2 d threads per piece: only at N near 2^30 with
+ *             segments of a prime number of chunks, whose pieces are one
+ *             chunk long).
  *   q, k, v   [B][H][N][d] of dt, 16-byte aligned
  *   slope     [H] fp32, the decay is exp(-slope[h]); any finite slope >= 0
  *   state_in  [B][H][d][d] fp32, or NULL for a zero initial state
@@ -315,8 +319,9 @@ size_t la_workspace_bytes(int op, la_dtype_t dt, int B, int H, int N, int d,
  *   nseq       1 .. 256 (more gives LA_ERR_UNSUPPORTED)
  *   cu_seqlens HOST array of nseq + 1 ints, read during the call only:
  *              cu_seqlens[0] = 0, non-decreasing (empty sequences allowed);
- *              T = cu_seqlens[nseq] is the packed length; H*T above 2^30
- *              gives LA_ERR_UNSUPPORTED
+ *              T = cu_seqlens[nseq] is the packed length; H*T above 2^30,
+ *              or pieces beyond 2^32 work-items (as for la_prefill), gives
+ *              LA_ERR_UNSUPPORTED
  *   q, k, v    [H][T][d] of dt (the B = 1 layout of la_prefill with the
  *              sequences back to back), 16-byte aligned
  *   slope      [H] fp32

@@ -72,6 +72,24 @@ def test_prefill_validation():
     assert prefill(ws=WSP + 8, wsb=nws) == ALIGN
 
 
+def test_piece_launch_limit():
+    # B*H*N within 2^30, but 131071 (a prime) chunks of 32 tokens per segment
+    # leave one-chunk pieces: 255 * 131071 piece workgroups of 256 threads
+    # exceed the dispatch's 32-bit count of work-items
+    N = 256 * 32 * 131071
+    assert N <= 2**30
+    far = [0x1000_0000_0000 * (i + 1) for i in range(5)]  # 16 TiB apart: no overlap
+    big = dict(B=1, H=1, N=N, d=128, C=32, q=far[0], k=far[1], v=far[2], o=far[3])
+    assert prefill(ws=far[4], wsb=2**62, **big) == UNSUP
+    bwd = la.lib().la_prefill_bwd(BF16, 1, 1, N, 128, 32, far[0], far[1], far[2], far[3], SLOPE,
+                                  None, far[4] + far[0], far[4] + far[1], far[4] + far[2],
+                                  far[4] + far[3], 2**62, None)
+    assert bwd == UNSUP
+    # with a segment of 2^17 chunks the pieces are 1024 tokens long: accepted
+    # (and then it needs a workspace)
+    assert prefill(**dict(big, N=2**30)) == WS
+
+
 def test_decode_validation():
     f = la.lib().la_decode_step
 
