@@ -82,7 +82,6 @@ __global__ __launch_bounds__(D / 32 * 64) void fwd_bf16_kernel(FwdPass p, PieceP
                                                                 const SeqTable st) {
   static_assert(!(STATE_ONLY && EPI), "the epilogue belongs to the main pass");
   using G = Cfg<C, D, STATE_ONLY>;
-  constexpr int kThreads = G::THREADS;
   constexpr int CT = G::CT;
 
   const int tid = threadIdx.x;
