@@ -4,8 +4,10 @@ reproduces the eager result bit for bit.
 
 Covered: the bf16 prefill with its segment pre-pass (three kernels on a
 caller's workspace), the allocation-free prefill (the entry point for callers
-under graph capture), the decode step (state updated in place) and a training
-step (forward, then the backward reusing the forward's workspace).  Outputs are
+under graph capture), the decode step (state updated in place), a training
+step (forward, then the backward reusing the forward's workspace), the gated
+prefill followed by multi-token decode, and a packed batch's forward and
+backward.  Outputs are
 set to NaN before each replay, so a replay that skipped a kernel would show.
 """
 import pytest
@@ -153,3 +155,61 @@ def test_training_step_replays():
     refs = (o.clone(), dq.clone(), dk.clone(), dv.clone())
     g = _capture(fn)
     _replay_and_check(g, (o, dq, dk, dv), refs)
+
+
+def test_gated_prefill_and_decode_tokens_replay():
+    dev = device()
+    q, k, v, sl = _prefill_inputs(dev, seed=8, H=8, N=4096)
+    B, H, N, d = q.shape
+    C = 128
+    gate = la_inputs.gate_device(8, B, H, N, d, dev, torch.bfloat16)
+    w = torch.from_numpy(la_inputs.norm_weight(8, H, d)).to(dev)
+    ws = torch.empty(la.workspace_bytes(0, la.LA_BF16, B, H, N, d, C), dtype=torch.uint8,
+                     device=dev)
+    y = torch.empty_like(q)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    # four new tokens per row on the final state of the prefill
+    K = 4
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    qt, kt, vt = ((torch.randn((B, H, K, d), generator=gen, device=dev) / d ** 0.5)
+                  .to(torch.bfloat16) for _ in range(3))
+    ot = torch.empty((B, H, K, d), dtype=torch.bfloat16, device=dev)
+
+    def fn():
+        la.prefill_gated(q, k, v, sl, gate, w, chunk=C, out=y, state_out=S, workspace=ws)
+        la.decode_tokens(qt, kt, vt, sl, S, out=ot)
+
+    fn()
+    torch.cuda.synchronize()
+    refs = (y.clone(), S.clone(), ot.clone())
+    g = _capture(fn)
+    _replay_and_check(g, (y, S, ot), refs)
+
+
+def test_packed_batch_forward_and_backward_replay():
+    dev = device()
+    H, d, C, T, nseq = 8, 128, 64, 6000, 7
+    cu = la_inputs.packed_cu_seqlens(9, nseq, T)
+    q, k, v = (x[0] for x in la_inputs.qkv_device(9, 1, H, T, d, dev, torch.bfloat16))
+    q, k, v = (x.contiguous() for x in (q, k, v))
+    gout = la_inputs.upstream_grad_device(9, 1, H, T, d, dev, torch.bfloat16)[0].contiguous()
+    sl = torch.from_numpy(la_inputs.slopes(H)).to(dev)
+    nws = max(la.workspace_bytes_varlen(0, la.LA_BF16, H, d, C, cu),
+              la.workspace_bytes_varlen(1, la.LA_BF16, H, d, C, cu))
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    S = torch.empty((nseq, H, d, d), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+
+    def fn():
+        la.prefill_varlen(q, k, v, sl, cu, chunk=C, out=o, state_out=S, workspace=ws)
+        la.prefill_bwd_varlen(q, k, v, gout, sl, cu, chunk=C, dq=dq, dk=dk, dv=dv, workspace=ws,
+                              reuse_forward_workspace=True)
+
+    fn()
+    torch.cuda.synchronize()
+    assert not torch.isnan(dq.float()).any()
+    refs = (o.clone(), S.clone(), dq.clone(), dk.clone(), dv.clone())
+    g = _capture(fn)
+    _replay_and_check(g, (o, S, dq, dk, dv), refs)
