@@ -195,7 +195,10 @@ __global__ __launch_bounds__(dec_threads<D>()) void decode_kernel(int H, int K, 
         const float ki = ks[j][ROWS * rg + m], qi = qs[j][ROWS * rg + m];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          sv[m][c] = fmaf(lam, sv[m][c], ki * v4[c]);
+          // in place (scale, then accumulate k v): the state keeps its
+          // registers from token to token, with no copies between them
+          sv[m][c] *= lam;
+          sv[m][c] = fmaf(ki, v4[c], sv[m][c]);
           acc[c] = fmaf(qi, sv[m][c], acc[c]);
         }
       }
