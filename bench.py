@@ -17,7 +17,8 @@ sequence, inputs resident in HBM.  The same line carries:
   * "prefill_gated": the same prefill with the fused output epilogue
     (per-head RMSNorm, weight, sigmoid gate);
   * "decode_tokens": 4 new tokens per (b, h) per call on the same state
-    (multi-token generation / draft verification), microseconds per call;
+    (multi-token generation / draft verification), microseconds per call,
+    and in "k16" the same with 16 tokens per call;
   * "train": forward + backward at B=4, H=16, N=32768, d=128, chunk 64;
   * "varlen": a packed batch of 64 ragged sequences (131072 tokens, H=32,
     d=128, chunk 128) continuing from per-sequence states, forward and
@@ -450,15 +451,16 @@ def bench_decode(args, torch, la, la_inputs):
     return res
 
 
-def bench_decode_tokens(args, torch, la, la_inputs):
-    """Multi-token decode: K = 4 new tokens per (b, h) per call on the B=64,
-    H=32, d=128 decode state, 250 consecutive calls with fresh q, k, v."""
-    B, H, d, K, calls = 64, 32, 128, 4, 250
+def _time_decode_tokens(torch, la, la_inputs, K, calls):
+    """Microseconds per la_decode_tokens call with K new tokens per (b, h) on
+    the B=64, H=32, d=128 decode state, over `calls` consecutive calls with
+    fresh q, k, v, and the algorithmic bytes of one call."""
+    B, H, d = 64, 32, 128
     dev = torch.device("cuda:0")
     slope = torch.from_numpy(la_inputs.slopes(H)).to(dev)
     S0 = torch.from_numpy(la_inputs.decode_state(3, B, H, d)).to(dev)
     g = torch.Generator(device=dev)
-    g.manual_seed(33)
+    g.manual_seed(33 + K)
     scale = 1.0 / d ** 0.5
     qs, ks, vs = (
         (torch.randn((calls, B, H, K, d), generator=g, device=dev) * scale).to(torch.bfloat16)
@@ -479,18 +481,32 @@ def bench_decode_tokens(args, torch, la, la_inputs):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / calls
     bytes_ = 2 * B * H * d * d * 4 + 4 * B * H * K * d * 2
+    del qs, ks, vs, S, S0
+    torch.cuda.empty_cache()
+    return us, bytes_
+
+
+def bench_decode_tokens(args, torch, la, la_inputs):
+    """Multi-token decode: K = 4 new tokens per (b, h) per call on the B=64,
+    H=32, d=128 decode state, 250 consecutive calls with fresh q, k, v; and
+    the same with K = 16 (the largest count the streaming kernel takes), 100
+    calls."""
+    B, H, d, K, calls = 64, 32, 128, 4, 250
+    us, bytes_ = _time_decode_tokens(torch, la, la_inputs, K, calls)
     achieved = bytes_ / (us * 1e-6) / 1e9
-    res = {
+    us16, bytes16 = _time_decode_tokens(torch, la, la_inputs, 16, 100)
+    achieved16 = bytes16 / (us16 * 1e-6) / 1e9
+    return {
         "B": B, "H": H, "d": d, "K": K, "calls": calls,
         "us_per_call": us,
         "tokens_per_s": B * K / (us * 1e-6),
         "roofline": {"kernel": "decode_kernel<128, bf16, 4> (la_decode_tokens)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "bytes_per_launch": bytes_},
+        "k16": {"K": 16, "calls": 100, "us_per_call": us16,
+                "tokens_per_s": B * 16 / (us16 * 1e-6),
+                "hbm_frac": achieved16 / HBM_PEAK_GBS, "bytes_per_launch": bytes16},
     }
-    del qs, ks, vs, S, S0
-    torch.cuda.empty_cache()
-    return res
 
 
 def bench_train(args, torch, la, la_inputs):
@@ -925,9 +941,10 @@ def main():
                 out["decode"]["us_per_step"], out["decode"]["graph"]["us_per_step"],
                 out["decode"]["cold"]["us_per_step"],
                 out["decode"]["stream_rmw_probe"]["nt_loads_sc1_stores_cold"]["GBs"]))
-        log("decode 4 tokens per call, B=64 ...")
+        log("decode 4 (and 16) tokens per call, B=64 ...")
         out["decode_tokens"] = bench_decode_tokens(args, torch, la, la_inputs)
-        log("  %.2f us/call" % out["decode_tokens"]["us_per_call"])
+        log("  %.2f us/call (16 tokens: %.2f us/call)" % (out["decode_tokens"]["us_per_call"],
+                                                         out["decode_tokens"]["k16"]["us_per_call"]))
     if args.only in (None, "train"):
         log("train fwd+bwd B=4 H=16 N=32K ...")
         out["train"] = bench_train(args, torch, la, la_inputs)
